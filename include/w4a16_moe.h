@@ -1,0 +1,196 @@
+/*
+ * w4a16_moe.h — C ABI of the MI355X (gfx950) W4A16 fused mixture-of-experts layer.
+ *
+ * The layer: BF16 activations routed top-k to experts whose weights are
+ * symmetric INT4 with one BF16 scale per group of 32 along the reduction
+ * dimension ("W4A16 그룹 스케일 형식", group-32 key: Chord page "vLLM 및 Novita AI,
+ * Kimi K2.x용 더 빠른 INT4 MoE 커널 출시: Chord", sections "vLLM과의 통합" and
+ * "런타임 고려사항"). Three stages run on the caller's HIP stream:
+ *
+ *   moe_align           topk_ids -> sorted_token_ids, expert_ids, num_tokens_post_padded
+ *   w4a16_moe_forward   gate_up GEMM + SiLU-and-mul, down GEMM, top-k weighted combine
+ *   w4a16_repack        once at weight load: canonical int4 + scales -> kernel layout
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller allocates and owns every buffer. Pointers named "device"
+ *   are device memory of the current HIP device; the library never allocates,
+ *   frees or synchronizes, and launches only on the given stream (`stream` is a
+ *   hipStream_t; NULL is the null stream). Calls are stateless apart from a
+ *   per-device cache of the compute-unit count, and are safe to capture in a
+ *   HIP graph (no host synchronization, no memset nodes).
+ * Errors: every function validates its arguments on the host before touching
+ *   the device and returns a w4a16_status. No fallback path exists: an
+ *   unsupported configuration is an error, never a silent switch (Chord page,
+ *   "vLLM과의 통합": unsupported quantization schemes raise instead of falling
+ *   back). W4A16_ERR_HIP means a HIP launch reported an error.
+ * Numerics: fp32 accumulation only; there is no f16-accumulation or
+ *   batch-invariant option (Chord page, "런타임 고려사항"; Humming PR page
+ *   "[vllm] vLLM에 고성능 JIT 양자화 커널 'Humming' 도입하기", section "코드 분석" 2).
+ * Routing ids outside [0, num_experts) mean "expert not resident in this call"
+ *   (one GPU's expert slice) and are skipped, not errors; weights are used as given.
+ * Dtypes: bf16 values travel as their uint16_t bit patterns.
+ */
+#ifndef W4A16_MOE_H
+#define W4A16_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
+  W4A16_ERR_UNSUPPORTED = 2, /* a valid request outside what the kernels implement */
+  W4A16_ERR_CAPACITY = 3,    /* sorted_token_ids buffer shorter than moe_align_capacity */
+  W4A16_ERR_WORKSPACE = 4,   /* workspace smaller than the matching *_workspace_bytes */
+  W4A16_ERR_HIP = 5          /* a HIP runtime call failed */
+} w4a16_status;
+
+/* Layer shape. group_size must be 32; hidden must be a multiple of 64 and
+ * intermediate a multiple of 32; 1 <= num_experts <= W4A16_MAX_EXPERTS. */
+typedef struct {
+  int32_t num_experts;  /* E: experts resident in this call */
+  int32_t hidden;       /* H */
+  int32_t intermediate; /* I: the gate_up projection has 2*I outputs */
+  int32_t group_size;   /* 32 */
+} w4a16_moe_shape;
+
+#define W4A16_GROUP_SIZE 32
+#define W4A16_MAX_EXPERTS 512
+#define W4A16_MAX_TOPK 32
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* w4a16_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Load time: weight repack                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of the two packed weight buffers written by w4a16_repack. They equal
+ * the canonical sizes (nibbles + scales), rearranged. */
+int w4a16_packed_bytes(const w4a16_moe_shape* shape, size_t* w13_bytes, size_t* w2_bytes);
+
+/* Rearrange canonical weights into the kernels' layout, once, before inference
+ * (the preprocessing step "validate, pad, repack into the target kernel's
+ * layout" of the Humming announcement, "Humming: vLLM과 Ant Group, 양자화 추론을
+ * 위한 범용 커널 라이브러리 오픈소스 공개", section "워크로드별 튜닝 및 JIT 컴파일";
+ * scales stored transposed for contiguous loads, Chord page "그룹 SM90 커널 기법").
+ *
+ * Canonical input (device):
+ *   w13_q  uint8  [E, 2I, H/2]  row r of W13: rows [0, I) gate, rows [I, 2I) up;
+ *                               element k in the low nibble of byte k/2 when k is
+ *                               even, high nibble otherwise; two's complement int4
+ *   w13_s  uint16 [E, 2I, H/32] bf16 scale of (row, group of 32 along H)
+ *   w2_q   uint8  [E, H, I/2]   down projection, same nibble convention
+ *   w2_s   uint16 [E, H, I/32]
+ * Output (device): w13_packed, w2_packed of the sizes from w4a16_packed_bytes.
+ * The packed layout is private to the library and may change between versions. */
+int w4a16_repack(const w4a16_moe_shape* shape, const uint8_t* w13_q, const uint16_t* w13_s,
+                 const uint8_t* w2_q, const uint16_t* w2_s, void* w13_packed, void* w2_packed,
+                 void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Token-to-expert alignment                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Length the caller must allocate for sorted_token_ids: T*topk + E*(block_m-1)
+ * (each expert can waste at most block_m-1 padding slots). expert_ids then has
+ * ceil(capacity / block_m) entries. Returns 0 for invalid arguments. */
+size_t moe_align_capacity(int32_t T, int32_t topk, int32_t num_experts, int32_t block_m);
+
+/* Device scratch bytes moe_align needs (0 for small inputs). */
+size_t moe_align_workspace_bytes(int32_t T, int32_t topk, int32_t num_experts, int32_t block_m);
+
+/* block_m for a call, from the expected routed tokens per expert (tok_e =
+ * T*topk/E_global): a tile sized by tokens-per-expert, not by total tokens
+ * (Chord page, "핵심 기여" and "인덱스 커널 기법": tok_e heuristic). Returns one
+ * of 16, 32, 64, 128; 0 for invalid arguments. */
+int32_t w4a16_choose_block_m(int32_t T, int32_t topk, int32_t num_experts_local, int32_t num_experts_global);
+
+/* Group the T*topk routed slots by expert, each expert padded to a multiple of
+ * block_m, into the over-allocated buffers the GEMMs read (vLLM's
+ * moe_align_block_size buffers, Chord page "런타임 고려사항"; the same output
+ * set as the FlashInfer Kimi-K3 fused router, page "[flashinfer] FlashInfer,
+ * B200 GPU에서 Kimi-K3 MoE 라우터 성능 최적화", section "코드 분석").
+ *
+ *   topk_ids               device int32 [T, topk]; ids outside [0, E) are skipped
+ *   block_m                16, 32, 64 or 128
+ *   sorted_token_ids       device int32 [capacity]: flat slot ids t*topk+j grouped
+ *                          by expert in ascending slot order; padding and the
+ *                          unused tail hold the sentinel T*topk
+ *   capacity               >= moe_align_capacity(T, topk, E, block_m)
+ *   expert_ids             device int32 [ceil(capacity/block_m)]: expert of each
+ *                          block_m-row block, -1 past the used blocks
+ *   num_tokens_post_padded device int32 [1]: sum over experts of ceil(count/block_m)*block_m
+ *   expert_counts          device int32 [E] or NULL: resident slots per expert
+ *   workspace              device, >= moe_align_workspace_bytes(...) bytes (may be
+ *                          NULL when that is 0); fully rewritten on every call
+ * The result is deterministic and unique (a stable counting sort). */
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t block_m,
+              int32_t* sorted_token_ids, int32_t capacity, int32_t* expert_ids,
+              int32_t* num_tokens_post_padded, int32_t* expert_counts, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The layer                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Device scratch bytes of w4a16_moe_forward: the bf16 SiLU-and-mul output
+ * h [capacity, I] and the fp32 per-slot down outputs y [T*topk, H]. */
+size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m);
+
+/* out[t, :] = bf16( sum_j [0 <= topk_ids[t,j] < E] * topk_weights[t,j] *
+ *                    W2[e] . bf16(silu(W13_gate[e] . x[t]) * (W13_up[e] . x[t])) )
+ * with e = topk_ids[t, j] and W = int4 * group scale, exactly (Chord page, TL;DR
+ * and "핵심 기여": the indexed W4A16 MoE operator; the top-k weight multiply and
+ * sum fused as moe_fused_mul_sum, Humming PR page, "왜 이게 좋은가" item 3).
+ *
+ *   x                  device bf16 [T, H]
+ *   topk_ids           device int32 [T, topk] (as given to moe_align)
+ *   topk_weights       device fp32 [T, topk]
+ *   sorted_token_ids, capacity, expert_ids, num_tokens_post_padded, block_m:
+ *                      moe_align's outputs for the same topk_ids and block_m; the
+ *                      padded count is read on the device (no host sync)
+ *   w13_packed, w2_packed  w4a16_repack's outputs for this shape
+ *   out                device bf16 [T, H]; every row is written (0 for tokens
+ *                      with no resident expert)
+ *   workspace          device, >= w4a16_moe_workspace_bytes(shape, T, topk, block_m)
+ * The shard profile is taken from the shapes alone; there is no shard argument
+ * (Chord page, "런타임 고려사항"). */
+int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                      const int32_t* topk_ids, const float* topk_weights,
+                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed,
+                      const void* w2_packed, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* The three stages of w4a16_moe_forward, callable one by one (same arguments
+ * and conventions; forward == gate_up, then down, then combine).
+ *
+ * gate_up: h[p, c] = bf16(silu(g[p, c]) * g[p, I + c]) for every real row p of
+ *   the aligned order (sorted_token_ids[p] < T*topk), g = x[sorted[p]/topk] . W13^T.
+ *   h: device bf16 [capacity, I]; padding rows are left untouched.
+ * down: y[sorted[p], n] = h[p, :] . W2[e, n, :] for every real row p, in fp32.
+ *   y: device fp32 [T*topk, H]; rows of non-resident slots are left untouched.
+ * combine: out[t, n] = bf16(sum_j resident(t, j) * topk_weights[t, j] * y[t*topk+j, n]),
+ *   summed in fp32 in j order. */
+int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed,
+                      uint16_t* h, void* stream);
+int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
+                   const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded, int32_t block_m, const void* w2_packed,
+                   float* y, void* stream);
+int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const int32_t* topk_ids,
+                      const float* topk_weights, const float* y, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_MOE_H */

@@ -95,14 +95,19 @@ def make_x(T: int, H: int, seed: int) -> np.ndarray:
     return to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
 
 
-def random_case(name, T, H, I, E, topk, block_m, seed, E_global=None, logit_bias=None) -> MoECase:
-    """Generic case: N(0,1) logits over E_global experts (default E), local slice [0, E)."""
+def random_case(name, T, H, I, E, topk, block_m, seed, E_global=None, logit_bias=None, weights=True) -> MoECase:
+    """Generic case: N(0,1) logits over E_global experts (default E), local slice [0, E).
+
+    weights=False skips x and the weights (routing-only cases for the alignment)."""
     Eg = E if E_global is None else E_global
     rng = np.random.default_rng(seed)
     logits = rng.standard_normal((T, Eg), dtype=np.float32)
     if logit_bias is not None:
         logits = (logits + logit_bias[None, :]).astype(np.float32)
     ids, w = route_topk(logits, topk)
+    if not weights:
+        return MoECase(name, T, H, I, E, topk, block_m, None, ids, w, None, None, None, None,
+                       meta={"E_global": Eg, "seed": seed})
     x = make_x(T, H, seed + 100)
     w13_q, w13_s, w2_q, w2_s = make_weights(E, H, I, seed + 200)
     return MoECase(name, T, H, I, E, topk, block_m, x, ids, w, w13_q, w13_s, w2_q, w2_s,
@@ -119,7 +124,7 @@ KIMI_H, KIMI_I, KIMI_E, KIMI_TOPK = 7168, 2048, 384, 8
 WORKLOADS = ("tiny", "decode_ep48", "islice_tp8", "prefill_contig48", "prefill_skew48", "prefill_skew48_identity")
 
 
-def contiguous_case(seed=4, T=768, E=48, H=KIMI_H, I=KIMI_I, topk=KIMI_TOPK, block_m=128) -> MoECase:
+def contiguous_case(seed=4, T=768, E=48, H=KIMI_H, I=KIMI_I, topk=KIMI_TOPK, block_m=128, weights=True) -> MoECase:
     """Every expert gets exactly T*topk/E slots; each token has topk distinct experts.
 
     Tokens are taken in groups of E/topk; each group splits a seeded permutation
@@ -133,6 +138,9 @@ def contiguous_case(seed=4, T=768, E=48, H=KIMI_H, I=KIMI_I, topk=KIMI_TOPK, blo
         perm = rng.permutation(E).astype(np.int32)
         ids[g0:g0 + per] = perm.reshape(per, topk)
     w = rng.dirichlet(np.ones(topk), size=T).astype(np.float32)
+    if not weights:
+        return MoECase("prefill_contig48", T, H, I, E, topk, block_m, None, ids, w, None, None, None, None,
+                       meta={"E_global": E, "seed": seed, "rows_per_expert": T * topk // E})
     x = make_x(T, H, seed + 100)
     w13_q, w13_s, w2_q, w2_s = make_weights(E, H, I, seed + 200)
     return MoECase("prefill_contig48", T, H, I, E, topk, block_m, x, ids, w, w13_q, w13_s, w2_q, w2_s,
@@ -145,23 +153,26 @@ def zipf_bias(E_global=KIMI_E, s=1.1, identity=False, perm_seed=0) -> np.ndarray
     return (-s * np.log(ranks)).astype(np.float32)
 
 
-def workload(name: str, block_m: int | None = None) -> MoECase:
-    """Build one of the named workloads. block_m None -> the workload's default."""
+def workload(name: str, block_m: int | None = None, weights: bool = True) -> MoECase:
+    """Build one of the named workloads. block_m None -> the workload's default.
+
+    weights=False builds the routing only (x and weights are None)."""
+    kw = dict(weights=weights)
     if name == "tiny":
-        c = random_case("tiny", T=16, H=256, I=128, E=8, topk=2, block_m=16, seed=1)
+        c = random_case("tiny", T=16, H=256, I=128, E=8, topk=2, block_m=16, seed=1, **kw)
     elif name == "decode_ep48":
         c = random_case("decode_ep48", T=128, H=KIMI_H, I=KIMI_I, E=48, topk=KIMI_TOPK, block_m=16, seed=2,
-                        E_global=KIMI_E)
+                        E_global=KIMI_E, **kw)
     elif name == "islice_tp8":
-        c = random_case("islice_tp8", T=512, H=KIMI_H, I=256, E=KIMI_E, topk=KIMI_TOPK, block_m=32, seed=3)
+        c = random_case("islice_tp8", T=512, H=KIMI_H, I=256, E=KIMI_E, topk=KIMI_TOPK, block_m=32, seed=3, **kw)
     elif name == "prefill_contig48":
-        c = contiguous_case()
+        c = contiguous_case(**kw)
     elif name == "prefill_skew48":
-        c = random_case("prefill_skew48", T=16384, H=KIMI_H, I=KIMI_I, E=48, topk=KIMI_TOPK, block_m=64, seed=5,
-                        E_global=KIMI_E, logit_bias=zipf_bias())
+        c = random_case("prefill_skew48", T=16384, H=KIMI_H, I=KIMI_I, E=48, topk=KIMI_TOPK, block_m=128, seed=5,
+                        E_global=KIMI_E, logit_bias=zipf_bias(), **kw)
     elif name == "prefill_skew48_identity":
         c = random_case("prefill_skew48_identity", T=16384, H=KIMI_H, I=KIMI_I, E=48, topk=KIMI_TOPK, block_m=128,
-                        seed=5, E_global=KIMI_E, logit_bias=zipf_bias(identity=True))
+                        seed=5, E_global=KIMI_E, logit_bias=zipf_bias(identity=True), **kw)
     else:
         raise KeyError(name)
     if block_m is not None:

@@ -1,0 +1,81 @@
+"""Helpers for the GPU tests: upload a synthetic case, run the library through
+the C ABI, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import w4a16_grouped_gemm_amd as w
+
+TOL = 2e-2  # |gpu - oracle| <= TOL * max(1, |oracle|), per element
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class DeviceCase:
+    """A MoECase resident on the GPU, weights repacked once."""
+
+    def __init__(self, case):
+        self.case = case
+        self.shape = w.make_shape(case.E, case.H, case.I)
+        n13, n2 = w.w4a16_packed_bytes(self.shape)
+        self.w13p = torch.empty(n13, dtype=torch.uint8, device="cuda")
+        self.w2p = torch.empty(n2, dtype=torch.uint8, device="cuda")
+        q13, s13, q2, s2 = (to_dev(case.w13_q), to_dev(case.w13_s), to_dev(case.w2_q), to_dev(case.w2_s))
+        w.w4a16_repack(self.shape, q13, s13, q2, s2, self.w13p, self.w2p)
+        torch.cuda.synchronize()
+        del q13, s13, q2, s2
+        self.x = to_dev(case.x)
+        self.ids = to_dev(case.topk_ids.astype(np.int32))
+        self.wts = to_dev(case.topk_weights.astype(np.float32))
+
+    def align(self, block_m, ids=None):
+        ids = self.ids if ids is None else ids
+        T, topk = ids.shape
+        buf = w.align_buffers(T, topk, self.case.E, block_m)
+        w.moe_align(ids, self.case.E, block_m, buf["sorted_token_ids"], buf["expert_ids"],
+                    buf["num_tokens_post_padded"], buf["expert_counts"], buf["workspace"])
+        return buf
+
+    def forward(self, block_m, ids=None, wts=None, x=None):
+        ids = self.ids if ids is None else ids
+        wts = self.wts if wts is None else wts
+        x = self.x if x is None else x
+        T, topk = ids.shape
+        buf = self.align(block_m, ids)
+        ws = torch.empty(max(1, w.w4a16_moe_workspace_bytes(self.shape, T, topk, block_m)), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.full((T, self.case.H), -1, dtype=torch.int16, device="cuda")  # poison: every row must be written
+        w.w4a16_moe_forward(self.shape, x, ids, wts, buf["sorted_token_ids"], buf["expert_ids"],
+                            buf["num_tokens_post_padded"], block_m, self.w13p, self.w2p, out, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16)
+
+
+def parity(gpu_bits: np.ndarray, ref: np.ndarray, what: str):
+    """Assert the per-element bound; return the max of |err| / tol."""
+    g = bf16_to_f64(gpu_bits)
+    tol = TOL * np.maximum(1.0, np.abs(ref))
+    err = np.abs(g - ref)
+    ratio = float((err / tol).max()) if err.size else 0.0
+    nfail = int((err > tol).sum())
+    bad = np.argwhere(err > tol)[:5].tolist()
+    say(f"  parity {what}: max err/tol {ratio:.4f}, fails {nfail}/{err.size}")
+    assert nfail == 0 and np.all(np.isfinite(g)), f"{what}: {nfail} elements out of tolerance, e.g. {bad}"
+    return ratio

@@ -1,0 +1,109 @@
+"""The C-ABI library builds, loads, exports every declared symbol, and rejects
+bad arguments on the host (no GPU needed: validation runs before any launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import w4a16_grouped_gemm_amd as w
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16_moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w.LIB_PATH):
+        from w4a16_grouped_gemm_amd import build
+        build.build()
+    return w.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    out = subprocess.run(["nm", "-D", "--defined-only", w.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert n in w._lib.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert w.w4a16_status_string(code) not in ("", "unknown status")
+    assert w.w4a16_status_string(99) == "unknown status"
+
+
+def test_sizes_and_heuristic(lib):
+    assert w.moe_align_capacity(3, 2, 4, 16) == 6 + 4 * 15
+    assert w.moe_align_capacity(0, 8, 48, 128) == 48 * 127
+    assert w.moe_align_capacity(3, 2, 4, 48) == 0  # unsupported block_m
+    assert w.moe_align_workspace_bytes(128, 8, 48, 16) == 0  # single-launch path
+    assert w.moe_align_workspace_bytes(16384, 8, 48, 128) > 0
+    s = w.make_shape(48, 7168, 2048)
+    q13, q2 = w.w4a16_packed_bytes(s)
+    assert q13 == 48 * 4096 * 7168 // 2 + 48 * 4096 * 224 * 2
+    assert q2 == 48 * 7168 * 2048 // 2 + 48 * 7168 * 64 * 2
+    cap = w.moe_align_capacity(128, 8, 48, 16)
+    assert w.w4a16_moe_workspace_bytes(s, 128, 8, 16) >= cap * 2048 * 2 + 128 * 8 * 7168 * 4
+    # tokens per expert drives the row-block size
+    assert w.w4a16_choose_block_m(128, 8, 48, 384) == 16
+    assert w.w4a16_choose_block_m(512, 8, 384, 384) == 32
+    assert w.w4a16_choose_block_m(768, 8, 48, 48) == 128
+    assert w.w4a16_choose_block_m(16384, 8, 48, 384) == 128
+    assert w.w4a16_choose_block_m(1, 8, 48, 384) == 16
+    assert w.w4a16_choose_block_m(8, 8, 48, 8) == 0  # local > global
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, shape, T=4, topk=2, cap=None, bm=16, ws_bytes=1 << 40, x=FAKE, ws=FAKE):
+    cap = w.moe_align_capacity(T, topk, shape.num_experts, bm) if cap is None else cap
+    return lib.w4a16_moe_forward(ctypes.byref(shape), x, T, topk, FAKE, FAKE, FAKE, cap, FAKE, FAKE, bm, FAKE, FAKE,
+                                 FAKE, ws, ws_bytes, None)
+
+
+def test_validation_status_codes(lib):
+    good = w.make_shape(8, 256, 128)
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.w4a16_packed_bytes(ctypes.byref(w.make_shape(8, 256, 128, 64)), ctypes.byref(a), ctypes.byref(b)) == 2
+    assert lib.w4a16_packed_bytes(None, ctypes.byref(a), ctypes.byref(b)) == 1
+    assert lib.w4a16_packed_bytes(ctypes.byref(good), None, None) == 1
+    for bad, code in [(w.make_shape(0, 256, 128), 1), (w.make_shape(8, 96, 128), 2), (w.make_shape(8, 256, 48), 2),
+                      (w.make_shape(513, 256, 128), 2), (w.make_shape(8, -64, 128), 1)]:
+        assert _fwd(lib, bad) == code, (bad.num_experts, bad.hidden, bad.intermediate)
+    assert _fwd(lib, good, bm=48) == 2                      # unsupported block_m
+    assert _fwd(lib, good, topk=33) == 2                     # topk above the maximum
+    assert _fwd(lib, good, T=-1) == 1
+    assert _fwd(lib, good, x=None) == 1                      # null activation
+    assert _fwd(lib, good, cap=w.moe_align_capacity(4, 2, 8, 16) - 1) == 3
+    assert _fwd(lib, good, ws_bytes=100) == 4
+    assert _fwd(lib, good, ws=None) == 4
+    # alignment
+    assert lib.moe_align(FAKE, 4, 2, 8, 16, FAKE, 10, FAKE, FAKE, None, None, 0, None) == 3
+    assert lib.moe_align(FAKE, 4, 2, 8, 24, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 2
+    assert lib.moe_align(None, 4, 2, 8, 16, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 1
+    cap = w.moe_align_capacity(16384, 8, 48, 128)
+    assert lib.moe_align(FAKE, 16384, 8, 48, 128, FAKE, cap, FAKE, FAKE, None, None, 0, None) == 4
+    # repack and stages
+    assert lib.w4a16_repack(ctypes.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, 3, FAKE, FAKE, 16, FAKE, FAKE, None) == 3
+    assert lib.w4a16_moe_down(ctypes.byref(good), 4, 2, None, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None) == 1
+
+
+def test_binding_raises(lib):
+    with pytest.raises(w.W4A16Error) as ei:
+        w.w4a16_packed_bytes(w.make_shape(8, 256, 128, 128))
+    assert ei.value.status == 2

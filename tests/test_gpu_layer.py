@@ -1,0 +1,113 @@
+"""GPU W4A16 MoE layer vs the CPU oracle: |gpu - oracle| <= 2e-2 * max(1, |oracle|)
+per element, on small cases in full and on the full-size workloads on sampled
+tokens (the oracle computes sampled rows one by one)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from _gpu import DeviceCase, parity, say, to_dev
+
+import w4a16_grouped_gemm_amd as w
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_rows(c, tokens=None, ids=None, wts=None):
+    ids = c.topk_ids if ids is None else ids
+    wts = c.topk_weights if wts is None else wts
+    return oracle.moe_layer(c.x, ids, wts, c.w13_q, c.w13_s, c.w2_q, c.w2_s, E=c.E, I=c.I, tokens=tokens)
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
+def test_tiny_all_block_sizes(block_m):
+    c = synthetic.workload("tiny")
+    say(f"layer tiny bm={block_m}")
+    d = DeviceCase(c)
+    parity(d.forward(block_m), oracle_rows(c), f"tiny bm{block_m}")
+
+
+SMALL = [
+    # name, T, H, I, E, topk, E_global, block_m
+    ("several tiles", 64, 512, 256, 16, 4, 16, 16),
+    ("ep slice, ragged", 77, 1024, 320, 12, 6, 24, 32),
+    ("k tail (G=18)", 40, 576, 96, 5, 3, 5, 16),
+    ("single token", 1, 256, 128, 8, 8, 8, 16),
+    ("bm64 skew", 150, 512, 160, 6, 2, 6, 64),
+    ("bm128", 300, 384, 128, 4, 2, 4, 128),
+    ("many experts", 96, 256, 64, 200, 8, 256, 16),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,topk,Eg,bm", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(name, T, H, I, E, topk, Eg, bm):
+    say(f"layer {name}: T={T} H={H} I={I} E={E} topk={topk} Eg={Eg} bm={bm}")
+    c = synthetic.random_case(name, T=T, H=H, I=I, E=E, topk=topk, block_m=bm, seed=T + H + I, E_global=Eg)
+    d = DeviceCase(c)
+    parity(d.forward(bm), oracle_rows(c), name)
+
+
+def test_tokens_without_resident_expert_are_zero():
+    c = synthetic.random_case("holes", T=50, H=256, I=64, E=6, topk=3, block_m=16, seed=7, E_global=30)
+    ids = c.topk_ids.copy()
+    ids[::4] = 29  # these tokens have no resident expert
+    ids[1, 0] = -1
+    d = DeviceCase(c)
+    out = d.forward(16, ids=to_dev(ids))
+    assert np.all(out[::4] == 0)
+    parity(out, oracle_rows(c, ids=ids), "holes")
+
+
+def test_stages_equal_forward_and_deterministic():
+    c = synthetic.random_case("stages", T=90, H=512, I=128, E=10, topk=4, block_m=32, seed=11, E_global=20)
+    d = DeviceCase(c)
+    ref = d.forward(32)
+    again = d.forward(32)
+    assert np.array_equal(ref, again)
+    buf = d.align(32)
+    cap = buf["sorted_token_ids"].numel()
+    h = torch.zeros((cap, c.I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((c.T * c.topk, c.H), dtype=torch.float32, device="cuda")
+    out = torch.full((c.T, c.H), -1, dtype=torch.int16, device="cuda")
+    w.w4a16_moe_gate_up(d.shape, d.x, c.T, c.topk, buf["sorted_token_ids"], buf["expert_ids"],
+                        buf["num_tokens_post_padded"], 32, d.w13p, h)
+    w.w4a16_moe_down(d.shape, c.T, c.topk, h, buf["sorted_token_ids"], buf["expert_ids"],
+                     buf["num_tokens_post_padded"], 32, d.w2p, y)
+    w.w4a16_moe_combine(d.shape, d.ids, d.wts, y, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), ref)
+
+
+def test_zero_tokens():
+    c = synthetic.random_case("empty", T=4, H=256, I=64, E=4, topk=2, block_m=16, seed=3)
+    d = DeviceCase(c)
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    wts = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, 256), dtype=torch.int16, device="cuda")
+    assert d.forward(16, ids=ids, wts=wts, x=x).shape == (0, 256)
+
+
+FULL = ["decode_ep48", "islice_tp8", "prefill_contig48", "prefill_skew48"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    say(f"layer full-size {name}: building inputs")
+    c = synthetic.workload(name)
+    d = DeviceCase(c)
+    say(f"layer full-size {name}: T={c.T} E={c.E} bm={c.block_m} slots={c.local_slots()}")
+    out = d.forward(c.block_m)
+    # sample tokens: the busiest, some with several resident slots, some with none, random others
+    rng = np.random.default_rng(0)
+    local = ((c.topk_ids >= 0) & (c.topk_ids < c.E)).sum(axis=1)
+    order = np.argsort(-local, kind="stable")
+    pick = set(order[:4].tolist()) | set(rng.choice(c.T, size=8, replace=False).tolist())
+    none = np.nonzero(local == 0)[0]
+    pick |= set(none[:2].tolist())
+    tokens = np.array(sorted(pick), np.int32)
+    ref = oracle_rows(c, tokens=tokens)
+    parity(out[tokens], ref, f"{name} ({len(tokens)} sampled tokens)")
+    assert np.all(out[none] == 0)
+    d2 = d.forward(c.block_m)
+    assert np.array_equal(out, d2), "run-to-run difference"

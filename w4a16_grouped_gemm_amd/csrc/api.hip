@@ -1,0 +1,234 @@
+// C ABI of the W4A16 MoE library: argument validation on the host, workspace
+// carving, and launch order on the caller's stream. Declarations, argument
+// meaning and error behaviour are documented in include/w4a16_moe.h.
+#include "w4a16_moe.h"
+
+#include <limits.h>
+
+#include "internal.h"
+
+using namespace w4a16;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool block_m_ok(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int check_shape(const w4a16_moe_shape* s) {
+  if (!s) return W4A16_ERR_INVALID_ARG;
+  if (s->num_experts < 1 || s->hidden < 1 || s->intermediate < 1) return W4A16_ERR_INVALID_ARG;
+  if (s->group_size != W4A16_GROUP_SIZE) return W4A16_ERR_UNSUPPORTED;
+  if (s->num_experts > W4A16_MAX_EXPERTS) return W4A16_ERR_UNSUPPORTED;
+  if (s->hidden % 64 != 0 || s->intermediate % 32 != 0) return W4A16_ERR_UNSUPPORTED;
+  // per-expert weight offsets and row products are computed in 64-bit; keep every
+  // index that stays 32-bit (rows, channels, groups) far from overflow
+  if (s->hidden > (1 << 20) || s->intermediate > (1 << 20)) return W4A16_ERR_UNSUPPORTED;
+  return W4A16_OK;
+}
+
+// T, topk and the derived sizes must fit the kernels' 32-bit slot indices.
+int check_tokens(int32_t T, int32_t topk, int32_t E, int32_t block_m) {
+  if (T < 0 || topk < 1 || E < 1) return W4A16_ERR_INVALID_ARG;
+  if (topk > W4A16_MAX_TOPK || E > W4A16_MAX_EXPERTS) return W4A16_ERR_UNSUPPORTED;
+  if (!block_m_ok(block_m)) return W4A16_ERR_UNSUPPORTED;
+  const int64_t cap = (int64_t)T * topk + (int64_t)E * (block_m - 1);
+  if (cap > INT_MAX / 2) return W4A16_ERR_UNSUPPORTED;
+  return W4A16_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+
+GemmParams gemm_params(const w4a16_moe_shape* s, int32_t T, int32_t topk, const int32_t* sorted, int32_t capacity,
+                       const int32_t* expert_ids, const int32_t* ntpp) {
+  GemmParams p{};
+  p.sorted = sorted;
+  p.expert_ids = expert_ids;
+  p.ntpp = ntpp;
+  p.E = s->num_experts;
+  p.topk = topk;
+  p.n_slots = T * topk;
+  p.capacity = capacity;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported configuration";
+    case W4A16_ERR_CAPACITY: return "sorted_token_ids capacity too small";
+    case W4A16_ERR_WORKSPACE: return "workspace too small";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_packed_bytes(const w4a16_moe_shape* shape, size_t* w13_bytes, size_t* w2_bytes) {
+  const int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  if (!w13_bytes || !w2_bytes) return W4A16_ERR_INVALID_ARG;
+  const size_t E = (size_t)shape->num_experts, H = (size_t)shape->hidden, I = (size_t)shape->intermediate;
+  // nibbles + scales, each region 256-byte aligned
+  *w13_bytes = round_up(E * 2 * I * H / 2) + round_up(E * 2 * I * (H / 32) * 2);
+  *w2_bytes = round_up(E * H * I / 2) + round_up(E * H * (I / 32) * 2);
+  return W4A16_OK;
+}
+
+int w4a16_repack(const w4a16_moe_shape* shape, const uint8_t* w13_q, const uint16_t* w13_s, const uint8_t* w2_q,
+                 const uint16_t* w2_s, void* w13_packed, void* w2_packed, void* stream) {
+  const int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  if (!w13_q || !w13_s || !w2_q || !w2_s || !w13_packed || !w2_packed) return W4A16_ERR_INVALID_ARG;
+  const int32_t E = shape->num_experts, H = shape->hidden, I = shape->intermediate;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* p13 = static_cast<uint8_t*>(w13_packed);
+  uint8_t* p2 = static_cast<uint8_t*>(w2_packed);
+  const size_t q13 = round_up((size_t)E * 2 * I * H / 2), q2 = round_up((size_t)E * H * I / 2);
+  hipError_t e = launch_repack(w13_q, w13_s, E, 2 * I, H, I, p13, reinterpret_cast<uint16_t*>(p13 + q13), s);
+  if (e != hipSuccess) return W4A16_ERR_HIP;
+  e = launch_repack(w2_q, w2_s, E, H, I, 0, p2, reinterpret_cast<uint16_t*>(p2 + q2), s);
+  return hip_status(e);
+}
+
+size_t moe_align_capacity(int32_t T, int32_t topk, int32_t num_experts, int32_t block_m) {
+  if (check_tokens(T, topk, num_experts, block_m) != W4A16_OK) return 0;
+  return (size_t)T * topk + (size_t)num_experts * (block_m - 1);
+}
+
+size_t moe_align_workspace_bytes(int32_t T, int32_t topk, int32_t num_experts, int32_t block_m) {
+  if (check_tokens(T, topk, num_experts, block_m) != W4A16_OK) return 0;
+  return align_workspace_bytes((int64_t)T * topk, num_experts);
+}
+
+int32_t w4a16_choose_block_m(int32_t T, int32_t topk, int32_t num_experts_local, int32_t num_experts_global) {
+  if (T < 0 || topk < 1 || num_experts_local < 1 || num_experts_global < num_experts_local) return 0;
+  // Expected routed tokens per expert. Row blocks must hold the typical
+  // busiest expert in one block while tokens are few (decode: weight streaming,
+  // each extra block re-reads the expert's weights), and grow to 128 rows once
+  // experts carry enough tokens to make the MFMA tile the limit.
+  const double tok_e = (double)T * topk / num_experts_global;
+  if (tok_e <= 6.0) return 16;
+  if (tok_e <= 14.0) return 32;
+  if (tok_e <= 40.0) return 64;
+  return 128;
+}
+
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t block_m,
+              int32_t* sorted_token_ids, int32_t capacity, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+              int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_tokens(T, topk, num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if ((T > 0 && !topk_ids) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
+    return W4A16_ERR_INVALID_ARG;
+  if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, num_experts, block_m)) return W4A16_ERR_CAPACITY;
+  const size_t ws = align_workspace_bytes((int64_t)T * topk, num_experts);
+  if (ws > 0 && (!workspace || workspace_bytes < ws)) return W4A16_ERR_WORKSPACE;
+  return hip_status(launch_align(topk_ids, T * topk, num_experts, block_m, sorted_token_ids, capacity, expert_ids,
+                                 num_tokens_post_padded, expert_counts, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m) {
+  if (check_shape(shape) != W4A16_OK) return 0;
+  if (check_tokens(T, topk, shape->num_experts, block_m) != W4A16_OK) return 0;
+  const size_t cap = moe_align_capacity(T, topk, shape->num_experts, block_m);
+  return round_up(cap * (size_t)shape->intermediate * 2) + round_up((size_t)T * topk * shape->hidden * 4);
+}
+
+int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed, uint16_t* h,
+                      void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  st = check_tokens(T, topk, shape->num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if ((T > 0 && !x) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w13_packed || !h)
+    return W4A16_ERR_INVALID_ARG;
+  if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
+    return W4A16_ERR_CAPACITY;
+  const int32_t E = shape->num_experts, H = shape->hidden, I = shape->intermediate;
+  GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded);
+  p.a = x;
+  p.wq = static_cast<const uint8_t*>(w13_packed);
+  p.ws = reinterpret_cast<const uint16_t*>(p.wq + round_up((size_t)E * 2 * I * H / 2));
+  p.out = h;
+  p.K = H;
+  p.N = 2 * I;
+  p.out_ld = I;
+  return hip_status(launch_moe_gemm(kGateUp, block_m, p, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
+                   const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded, int32_t block_m, const void* w2_packed, float* y,
+                   void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  st = check_tokens(T, topk, shape->num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if (!h || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w2_packed || (T > 0 && !y))
+    return W4A16_ERR_INVALID_ARG;
+  if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
+    return W4A16_ERR_CAPACITY;
+  const int32_t E = shape->num_experts, H = shape->hidden, I = shape->intermediate;
+  GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded);
+  p.a = h;
+  p.wq = static_cast<const uint8_t*>(w2_packed);
+  p.ws = reinterpret_cast<const uint16_t*>(p.wq + round_up((size_t)E * H * I / 2));
+  p.out = y;
+  p.K = I;
+  p.N = H;
+  p.out_ld = H;
+  return hip_status(launch_moe_gemm(kDown, block_m, p, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const int32_t* topk_ids,
+                      const float* topk_weights, const float* y, uint16_t* out, void* stream) {
+  const int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  if (T < 0 || topk < 1) return W4A16_ERR_INVALID_ARG;
+  if (topk > W4A16_MAX_TOPK) return W4A16_ERR_UNSUPPORTED;
+  if ((int64_t)T * topk > INT_MAX / 2) return W4A16_ERR_UNSUPPORTED;
+  if (T > 0 && (!topk_ids || !topk_weights || !y || !out)) return W4A16_ERR_INVALID_ARG;
+  return hip_status(launch_combine(topk_ids, topk_weights, y, out, T, topk, shape->hidden, shape->num_experts,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                      const int32_t* topk_ids, const float* topk_weights, const int32_t* sorted_token_ids,
+                      int32_t capacity, const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                      int32_t block_m, const void* w13_packed, const void* w2_packed, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  st = check_tokens(T, topk, shape->num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if ((T > 0 && (!x || !topk_ids || !topk_weights || !out)) || !sorted_token_ids || !expert_ids ||
+      !num_tokens_post_padded || !w13_packed || !w2_packed)
+    return W4A16_ERR_INVALID_ARG;
+  if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
+    return W4A16_ERR_CAPACITY;
+  const size_t need = w4a16_moe_workspace_bytes(shape, T, topk, block_m);
+  if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  if (T == 0) return W4A16_OK;
+  // workspace: h [cap_min, I] bf16, then y [T*topk, H] fp32
+  const size_t cap_min = moe_align_capacity(T, topk, shape->num_experts, block_m);
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  float* y = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + round_up(cap_min * shape->intermediate * 2));
+  // Rows past cap_min are never live: num_tokens_post_padded <= cap_min.
+  st = w4a16_moe_gate_up(shape, x, T, topk, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
+                         block_m, w13_packed, h, stream);
+  if (st != W4A16_OK) return st;
+  st = w4a16_moe_down(shape, T, topk, h, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
+                      block_m, w2_packed, y, stream);
+  if (st != W4A16_OK) return st;
+  return w4a16_moe_combine(shape, T, topk, topk_ids, topk_weights, y, out, stream);
+}
+
+}  // extern "C"

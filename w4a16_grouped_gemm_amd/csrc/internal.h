@@ -1,0 +1,74 @@
+// Internal declarations of the gfx950 W4A16 MoE library: kernel launchers
+// called by the C ABI in api.hip, and the packed-weight layout they share.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (written once by the repack kernels, read by the GEMMs)
+//
+// A projection W of one expert has N output channels and a reduction length
+// K = 32 * G. Channels are taken in n-blocks of 64, each split into four
+// 16-wide column blocks c = 0..3, which is the B-operand width of
+// v_mfma_f32_16x16x32_bf16. For gate_up (N = 2I) an n-block nb holds gate
+// channels 32nb..32nb+31 in c = 0, 1 and the matching up channels
+// I+32nb..I+32nb+31 in c = 2, 3, so one wave sees both halves of SiLU-and-mul.
+//
+// Nibbles: one 1024-byte unit per (expert e, n-block nb, group g), units ordered
+// e-major, then nb, then g (one n-block streams all of K contiguously). In a
+// unit, lane l (0..63) owns bytes [16 l, 16 l + 16): dword c holds the eight
+// codes of column 16c + (l & 15), k = 32g + 8(l >> 4) + 0..7, with element
+// 2j in bits [4j, 4j+4) and element 2j+1 in bits [16+4j, 20+4j), j = 0..3.
+// A code is the weight's int4 value plus 8 (0..15), so OR-ing it into the
+// mantissa of bf16 128.0 (0x4300) yields the exact bf16 value q + 136.
+//
+// Scales: one 64-entry unit of bf16 per (e, nb, g), same unit order; entry
+// 4 * (l & 15) + c is the scale of column 16c + (l & 15), so a lane reads its
+// four scales as one 8-byte load.
+// ---------------------------------------------------------------------------
+constexpr int kGroup = 32;
+constexpr int kNBlock = 64;
+constexpr int kNibUnitBytes = 1024;
+constexpr int kScaleUnitElems = 64;
+
+struct GemmParams {
+  const uint16_t* a;       // gate_up: x [T, H]; down: h [capacity, I]
+  const uint8_t* wq;       // packed nibbles of this projection, all experts
+  const uint16_t* ws;      // packed scales of this projection, all experts
+  const int32_t* sorted;   // sorted_token_ids [capacity]
+  const int32_t* expert_ids;
+  const int32_t* ntpp;     // num_tokens_post_padded (device)
+  void* out;               // gate_up: h bf16 [capacity, I]; down: y fp32 [n_slots, H]
+  int32_t K;               // reduction length (H or I)
+  int32_t N;               // output channels (2I or H)
+  int32_t E;
+  int32_t topk;
+  int32_t n_slots;         // T * topk: ids >= this are padding
+  int32_t capacity;
+  int32_t out_ld;          // leading dimension of out (I or H)
+};
+
+enum GemmMode { kGateUp = 0, kDown = 1 };
+
+// Launchers: return hipSuccess or the launch error. All run on `stream`.
+hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t block_m, int32_t* sorted,
+                        int32_t capacity, int32_t* expert_ids, int32_t* ntpp, int32_t* counts,
+                        void* workspace, hipStream_t stream);
+size_t align_workspace_bytes(int64_t n, int32_t E);
+
+hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t N, int32_t K,
+                         int32_t interleave_I, uint8_t* out_q, uint16_t* out_s, hipStream_t stream);
+
+hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream);
+
+hipError_t launch_combine(const int32_t* ids, const float* w, const float* y, uint16_t* out, int32_t T,
+                          int32_t topk, int32_t H, int32_t E, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace w4a16
