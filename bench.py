@@ -9,10 +9,13 @@ before timing starts; weight repack is load time and is not timed.
 Timing follows the pages' kernel-benchmark method (Humming announcement,
 "Humming: vLLM과 Ant Group, 양자화 추론을 위한 범용 커널 라이브러리 오픈소스 공개",
 section "결과: 커널 마이크로벤치마크": warmed up, cold L2, each sample timed on
-its own): before every timed step a 1 GiB buffer is rewritten to push the
-layer's data out of L2 and the 256 MB Infinity Cache, outside the timed
-interval. Each step is timed with HIP events on the stream the kernels run
-on, with events between the stages for the per-kernel breakdown.
+its own): before every timed step a 1 GiB buffer is *read* (a sum), outside
+the timed interval, which pushes the layer's data out of L2 and the 256 MB
+Infinity Cache and leaves them clean. (A write-based flush would leave up to
+256 MB of dirty lines whose write-back then lands inside the timed kernel and
+halves its read bandwidth.) Each step is timed with HIP events on the stream
+the kernels run on, with events between the stages for the per-kernel
+breakdown.
 
 Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -152,7 +155,10 @@ def main():
     y_off = ((cap * I * 2 + 255) // 256) * 256
     y = ws[y_off: y_off + T * topk * H * 4].view(torch.float32).view(T * topk, H)
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")  # 1 GiB, read to evict caches
+
+    def flush():
+        flush_buf.sum()
 
     def align():
         w.moe_align(ids, E, bm, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"], None,
@@ -189,7 +195,7 @@ def main():
 
     for _ in range(args.warmup):
         if not args.warm:
-            flush.fill_(1)
+            flush()
         forward_step(mk(2))
         stages(mk(5))
     torch.cuda.synchronize()
@@ -200,7 +206,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         if not args.warm:
-            flush.fill_(i & 0xFF)
+            flush()
         ev = mk(2)
         forward_step(ev)
         layer_ev.append(ev)
@@ -208,7 +214,7 @@ def main():
     wall = time.perf_counter() - t0
     for i in range(args.steps):
         if not args.warm:
-            flush.fill_(i & 0xFF)
+            flush()
         ev = mk(5)
         stages(ev)
         stage_ev.append(ev)
@@ -249,7 +255,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": c.name, "T": T, "hidden": H, "intermediate": I, "experts_local": E,
                    "experts_global": Eg, "topk": topk, "block_m": bm, "resident_slots": work["S"],
-                   "active_experts": work["active"], "cache": "warm" if args.warm else "cold (1 GiB flush per step)"},
+                   "active_experts": work["active"], "cache": "warm" if args.warm else "cold (1 GiB read before each step)"},
         "layer_GBps": round(layer_gbps, 1),
         "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
         "layer_TFLOPs": round(layer_tflops, 2),

@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16_moe.so")
+# W4A16_MOE_LIB may point at another build of the same library (A/B timing)
+LIB_PATH = os.environ.get("W4A16_MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libw4a16_moe.so")
 
 _lib = None
 

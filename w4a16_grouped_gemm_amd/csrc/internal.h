@@ -65,6 +65,11 @@ hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t
 
 hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream);
 
+// Tiled (LDS-staged, 128 x 256 tile) variant for block_m == 128; used by
+// launch_moe_gemm when the shape fits it.
+bool tiled_gemm_supported(int32_t block_m, const GemmParams& p);
+hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, hipStream_t stream);
+
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* y, uint16_t* out, int32_t T,
                           int32_t topk, int32_t H, int32_t E, hipStream_t stream);
 

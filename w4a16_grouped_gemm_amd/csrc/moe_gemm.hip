@@ -20,11 +20,16 @@
 //
 // Work decomposition. A work unit is (block_m-row block mb, 64-channel n-block
 // nb), computed by one wave over the whole reduction: the unit's packed weights
-// are one contiguous stream (K/32 KiB of nibbles plus K/16 scales bytes per
-// 64 channels). Waves are persistent: a grid sized to the resident wave count
-// strides over units, and the number of live row blocks is read from
-// num_tokens_post_padded on the device, so the over-allocated alignment buffer
-// costs nothing (Chord page, "런타임 고려사항").
+// are one contiguous stream (K/32 KiB of nibbles plus K/16 scale bytes per
+// 64 channels). Waves are persistent: the grid is sized to the resident wave
+// count, the number of live row blocks is read from num_tokens_post_padded on
+// the device (so the over-allocated alignment buffer costs nothing; Chord page,
+// "런타임 고려사항"), and the live units are split evenly over the waves.
+//
+// Latency hiding. Each wave keeps two batches of U groups in registers and
+// issues the loads of one while it computes the other; sched_barrier pins
+// that order against the scheduler, and the batch offset is made opaque so the
+// look-ahead load is not re-materialized next to its use.
 #include "internal.h"
 
 #include <algorithm>
@@ -39,18 +44,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kCodeMask = 0x000F000Fu;
-constexpr uint32_t kBf16_128 = 0x43004300u;    // two bf16 128.0
+constexpr uint32_t kBf16_128 = 0x43004300u;       // two bf16 128.0
 constexpr uint32_t kBf16_Minus136 = 0xC308C308u;  // two bf16 -136.0
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Eight stored codes (q + 8) -> eight exact bf16 values q + 136, k-order.
-__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w) {
+// (a & mask) | magic in one VALU op. gfx9 VOP3 takes no literal and at most one
+// scalar operand, so the mask comes from an SGPR and the magic from a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Eight stored codes (q + 8) -> eight exact bf16 values q + 136, in k order.
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w, uint32_t magic) {
   u32x4 r;
-  r.x = (w & kCodeMask) | kBf16_128;
-  r.y = ((w >> 4) & kCodeMask) | kBf16_128;
-  r.z = ((w >> 8) & kCodeMask) | kBf16_128;
-  r.w = ((w >> 12) & kCodeMask) | kBf16_128;
+  r.x = and_or(w, kCodeMask, magic);
+  r.y = and_or(w >> 4, kCodeMask, magic);
+  r.z = and_or(w >> 8, kCodeMask, magic);
+  r.w = and_or(w >> 12, kCodeMask, magic);
   return as_bf16x8(r);
 }
 
@@ -61,76 +74,146 @@ __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
-// RB row blocks of 16 (block_m = 16 RB); U groups of 32 loaded per batch.
-template <int MODE, int RB, int U>
+// Registers of U consecutive 32-wide groups for one wave: its 16-byte nibble
+// chunk and 8-byte scale chunk per group, and its A fragment per row block.
+template <int RB, int U>
+struct Batch {
+  u32x4 nib[U];
+  u32x2 sc[U];
+  u32x4 a[RB][U];
+};
+
+// Per-wave stream pointers: wave-uniform bases (SGPRs) plus fixed per-lane offsets.
+template <int RB>
+struct Streams {
+  const uint8_t* wq;  // nibble units of this (expert, n-block), uniform
+  const uint8_t* ws;  // scale units, uniform
+  uint32_t q_lane;    // 16 * lane
+  uint32_t s_lane;    // 8 * (lane & 15)
+  const uint8_t* a[RB];  // this lane's A row (+ its 8-element k offset)
+};
+
+// Loads groups [g0, g0 + U). g0 is made opaque to the optimizer so that a
+// prefetch issued one batch early is not re-materialized at its use.
+template <int RB, int U>
+__device__ __forceinline__ void load_batch(Batch<RB, U>& b, const Streams<RB>& st, int g0) {
+  asm volatile("" : "+s"(g0));
+  const uint8_t* q = st.wq + (int64_t)g0 * kNibUnitBytes + st.q_lane;
+  const uint8_t* sc = st.ws + (int64_t)g0 * (kScaleUnitElems * 2) + st.s_lane;
+#pragma unroll
+  for (int uu = 0; uu < U; ++uu) {
+    b.nib[uu] = *reinterpret_cast<const u32x4*>(q + uu * kNibUnitBytes);
+    b.sc[uu] = *reinterpret_cast<const u32x2*>(sc + uu * (kScaleUnitElems * 2));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      b.a[rb][uu] = *reinterpret_cast<const u32x4*>(st.a[rb] + (int64_t)(g0 + uu) * (kGroup * 2));
+  }
+}
+
+// acc[rb][c] += s_c * (sum over the group of a * q): one correction MFMA per
+// row block, four code MFMAs, four FMAs per output.
+template <int RB, int U>
+__device__ __forceinline__ void compute_batch(const Batch<RB, U>& b, floatx4 (&acc)[RB][4], uint32_t magic,
+                                              bf16x8 minus136) {
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int uu = 0; uu < U; ++uu) {
+    const float s[4] = {bf16_lo(b.sc[uu].x), bf16_hi(b.sc[uu].x), bf16_lo(b.sc[uu].y), bf16_hi(b.sc[uu].y)};
+    bf16x8 w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = codes_to_bf16(b.nib[uu][c], magic);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bf16x8 a = as_bf16x8(b.a[rb][uu]);
+      const floatx4 corr = mfma16(a, minus136, zero4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[rb][c] += s[c] * mfma16(a, w[c], corr);
+    }
+  }
+}
+
+// RB row blocks of 16 (block_m = 16 RB); batches of U groups; NS batches in
+// registers: while one is computed the loads of the next NS - 1 are in flight.
+template <int MODE, int RB, int U, int NS>
 __global__ __launch_bounds__(256) void moe_gemm_stream_kernel(GemmParams p) {
   constexpr int BM = 16 * RB;
   const int lane = (int)threadIdx.x & 63;
-  const int wave = (int)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+  const int wave = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nwaves = (int)gridDim.x * 4;
   const int ntpp = min(*p.ntpp, p.capacity);
   const int n_mblocks = ntpp / BM;
   const int NB = p.N / kNBlock;
   const int G = p.K / kGroup;
+  const int nbatch = G / U;  // pipelined full batches; groups [nbatch * U, G) are the tail
   const int units = n_mblocks * NB;
-  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  uint32_t magic = kBf16_128;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
   const bf16x8 minus136 = as_bf16x8(u32x4{kBf16_Minus136, kBf16_Minus136, kBf16_Minus136, kBf16_Minus136});
 
-  for (int u = wave; u < units; u += nwaves) {
+  // Balanced static split: every active wave takes the same number of
+  // consecutive units (consecutive n-blocks of one row block share A rows).
+  const int per_wave = (units + nwaves - 1) / nwaves;
+  const int u_begin = wave * per_wave;
+  const int u_end = min(units, u_begin + per_wave);
+  for (int u = u_begin; u < u_end; ++u) {
     const int mb = u / NB;
     const int nb = u - mb * NB;
     const int e = p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;
 
-    const u32x4* arow[RB];
-    bool real[RB];
+    // A rows. A padding row reads the block's first row (always a real one, so
+    // all padding lanes share one address); its results land only in that
+    // row of the tile, which is never stored.
+    Streams<RB> st;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int prow = mb * BM + rb * 16 + (lane & 15);
       const int id = p.sorted[prow];
-      real[rb] = (unsigned)id < (unsigned)p.n_slots;
-      const int64_t src = (MODE == kGateUp) ? (real[rb] ? id / p.topk : 0) : prow;
-      arow[rb] = reinterpret_cast<const u32x4*>(p.a + src * p.K + 8 * (lane >> 4));
+      const bool real = (unsigned)id < (unsigned)p.n_slots;
+      int64_t src;
+      if (MODE == kGateUp) {
+        const int id0 = p.sorted[mb * BM];
+        src = (real ? id : id0) / p.topk;
+      } else {
+        src = real ? prow : mb * BM;
+      }
+      st.a[rb] = reinterpret_cast<const uint8_t*>(p.a + src * p.K + 8 * (lane >> 4));
     }
     const int64_t unit0 = ((int64_t)e * NB + nb) * G;
-    const u32x4* wq = reinterpret_cast<const u32x4*>(p.wq + unit0 * kNibUnitBytes) + lane;
-    const u32x2* ws = reinterpret_cast<const u32x2*>(p.ws + unit0 * kScaleUnitElems) + (lane & 15);
+    st.wq = p.wq + unit0 * kNibUnitBytes;
+    st.ws = reinterpret_cast<const uint8_t*>(p.ws + unit0 * kScaleUnitElems);
+    st.q_lane = 16u * (uint32_t)lane;
+    st.s_lane = 8u * (uint32_t)(lane & 15);
 
     floatx4 acc[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[rb][c] = zero4;
+      for (int c = 0; c < 4; ++c) acc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    for (int g0 = 0; g0 < G; g0 += U) {
-      u32x4 nib[U];
-      u32x2 sc[U];
-      u32x4 av[RB][U];
+    if (nbatch > 0) {
+      Batch<RB, U> b[NS];
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int g = g0 + uu;
-        const bool ok = g < G;
-        nib[uu] = ok ? wq[(int64_t)g * 64] : u32x4{0u, 0u, 0u, 0u};
-        sc[uu] = ok ? ws[(int64_t)g * 16] : u32x2{0u, 0u};
+      for (int j = 0; j < NS - 1; ++j) load_batch(b[j], st, min(j, nbatch - 1) * U);
+      for (int i = 0; i < nbatch; i += NS) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) av[rb][uu] = (ok && real[rb]) ? arow[rb][g * 4] : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const float s[4] = {bf16_lo(sc[uu].x), bf16_hi(sc[uu].x), bf16_lo(sc[uu].y), bf16_hi(sc[uu].y)};
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const bf16x8 a = as_bf16x8(av[rb][uu]);
-          const floatx4 corr = mfma16(a, minus136, zero4);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const floatx4 part = mfma16(a, codes_to_bf16(nib[uu][c]), corr);
-            acc[rb][c] += s[c] * part;
-          }
+        for (int j = 0; j < NS; ++j) {
+          // look-ahead NS - 1 batches; past the end it re-reads the last batch
+          load_batch(b[(j + NS - 1) % NS], st, min(i + j + NS - 1, nbatch - 1) * U);
+          __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead loads ahead of the math
+          if (i + j < nbatch) compute_batch(b[j], acc, magic, minus136);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
+    for (int g = nbatch * U; g < G; ++g) {
+      Batch<RB, 1> t;
+      load_batch(t, st, g);
+      compute_batch(t, acc, magic, minus136);
     }
 
     // Epilogue. Output element i of a 16x16 tile sits at row 4 (lane >> 4) + i,
@@ -184,14 +267,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 
 std::atomic<int> g_cu_count[64];
 
-template <int MODE, int RB, int U>
+template <int MODE, int RB, int U, int NS>
 hipError_t launch_stream(const GemmParams& p, hipStream_t stream) {
   constexpr int BM = 16 * RB;
   const int64_t units_max = (int64_t)(p.capacity / BM) * (p.N / kNBlock);
   if (units_max == 0) return hipSuccess;
   static int blocks_per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_kernel<MODE, RB, U>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_kernel<MODE, RB, U, NS>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
     return n;
@@ -199,17 +282,17 @@ hipError_t launch_stream(const GemmParams& p, hipStream_t stream) {
   const int64_t resident_waves = (int64_t)device_cu_count() * blocks_per_cu * 4;
   const int64_t waves = std::min(units_max, resident_waves);
   const int grid = (int)((waves + 3) / 4);
-  hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, RB, U>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, RB, U, NS>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_mode(int block_m, const GemmParams& p, hipStream_t stream) {
   switch (block_m) {
-    case 16: return launch_stream<MODE, 1, 8>(p, stream);
-    case 32: return launch_stream<MODE, 2, 4>(p, stream);
-    case 64: return launch_stream<MODE, 4, 2>(p, stream);
-    case 128: return launch_stream<MODE, 8, 1>(p, stream);
+    case 16: return launch_stream<MODE, 1, 4, 2>(p, stream);
+    case 32: return launch_stream<MODE, 2, 2, 2>(p, stream);
+    case 64: return launch_stream<MODE, 4, 1, 2>(p, stream);
+    case 128: return launch_stream<MODE, 8, 1, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -228,6 +311,7 @@ int device_cu_count() {
 }
 
 hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream) {
+  if (tiled_gemm_supported(block_m, p)) return launch_moe_gemm_tiled(mode, p, stream);
   return mode == kGateUp ? launch_mode<kGateUp>(block_m, p, stream) : launch_mode<kDown>(block_m, p, stream);
 }
 
