@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slots", type=int, default=64, help="resident slots the CPU baseline computes")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -269,6 +271,14 @@ def main():
         "roofline": roof,
         "source_hash": kernel_source_hash(),
     }
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        flush()
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = 1 << 28
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_slots)
