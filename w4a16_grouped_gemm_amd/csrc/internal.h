@@ -70,6 +70,11 @@ hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, 
 bool tiled_gemm_supported(int32_t block_m, const GemmParams& p);
 hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, hipStream_t stream);
 
+// Weight-streaming variant for block_m 16..64 with LDS rings for A and scales;
+// used when N is a multiple of 256 and K / 32 a multiple of 4.
+bool stream_lds_supported(int32_t block_m, const GemmParams& p);
+hipError_t launch_moe_gemm_stream_lds(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream);
+
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* y, uint16_t* out, int32_t T,
                           int32_t topk, int32_t H, int32_t E, hipStream_t stream);
 

@@ -106,8 +106,9 @@ __device__ __forceinline__ void load_batch(Batch<RB, U>& b, const Streams<RB>& s
   const uint8_t* sc = st.ws + (int64_t)g0 * (kScaleUnitElems * 2) + st.s_lane;
 #pragma unroll
   for (int uu = 0; uu < U; ++uu) {
-    b.nib[uu] = *reinterpret_cast<const u32x4*>(q + uu * kNibUnitBytes);
-    b.sc[uu] = *reinterpret_cast<const u32x2*>(sc + uu * (kScaleUnitElems * 2));
+    // weights are read once: non-temporal loads keep them out of the way of reused data
+    b.nib[uu] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + uu * kNibUnitBytes));
+    b.sc[uu] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sc + uu * (kScaleUnitElems * 2)));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
       b.a[rb][uu] = *reinterpret_cast<const u32x4*>(st.a[rb] + (int64_t)(g0 + uu) * (kGroup * 2));
@@ -312,6 +313,7 @@ int device_cu_count() {
 
 hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream) {
   if (tiled_gemm_supported(block_m, p)) return launch_moe_gemm_tiled(mode, p, stream);
+  if (stream_lds_supported(block_m, p)) return launch_moe_gemm_stream_lds(mode, block_m, p, stream);
   return mode == kGateUp ? launch_mode<kGateUp>(block_m, p, stream) : launch_mode<kDown>(block_m, p, stream);
 }
 

@@ -1,0 +1,287 @@
+// Weight-streaming W4A16 expert GEMM for few tokens per expert (block_m 16 to 64).
+//
+// With a few routed tokens per expert the layer is a weight stream: every
+// byte of each active expert's packed weights is read once, and the kernel's
+// job is to keep enough of them in flight to run HBM at full rate (decode is
+// HBM-bound; Chord page "vLLM 및 Novita AI, Kimi K2.x용 더 빠른 INT4 MoE 커널
+// 출시: Chord", "핵심 기여" and the latency-tuned buffered-K depth of "그룹 SM90
+// 커널 기법"). The arithmetic is the same as the tiled kernel's: exact integer
+// operands q + 136 on v_mfma_f32_16x16x32_bf16, a -136 * sum(x) correction in
+// the C input, one fp32 FMA per output per 32-wide group for the BF16 scale.
+//
+// Work unit: (row block of block_m rows, four consecutive 64-channel n-blocks)
+// for one 256-thread workgroup; wave w streams n-block 4 ng + w over the whole
+// reduction. Only the weight nibbles are held in registers: a ring of kDepth
+// batches of U groups, so kDepth - 1 batches (kDepth - 1 KiB x U per wave) are
+// in flight while one is computed. The row block's A fragments (gathered
+// activation rows, shared by the four waves) and each wave's group scales go
+// global -> LDS by global_load_lds (no registers in flight) into rings of the
+// same depth. Copies and loads of a batch are issued together, so the in-order
+// vmcnt covers them all: a wave waits for its own batch, then a fence-free
+// barrier publishes every wave's A copies and proves the slot refilled next
+// has been consumed.
+#include "internal.h"
+
+#include <algorithm>
+
+namespace w4a16 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kThreads = 256;
+constexpr int kUnitNBlocks = 4;  // n-blocks per workgroup unit (one per wave)
+// Weights are read exactly once: non-temporal loads keep them from displacing
+// reused data in L2 / Infinity Cache and raised a streaming read from 5.8 to
+// 6.4 TB/s in a probe. (Cache-policy operand of global_load_lds: 2 = nt.)
+constexpr int kNonTemporal = 2;
+constexpr uint32_t kCodeMask = 0x000F000Fu;
+constexpr uint32_t kBf16_128 = 0x43004300u;
+constexpr uint32_t kBf16_Minus136 = 0xC308C308u;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w, uint32_t magic) {
+  u32x4 r;
+  r.x = and_or(w, kCodeMask, magic);
+  r.y = and_or(w >> 4, kCodeMask, magic);
+  r.z = and_or(w >> 8, kCodeMask, magic);
+  r.w = and_or(w >> 12, kCodeMask, magic);
+  return as_bf16x8(r);
+}
+
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int RB, int U, int DEPTH>
+struct Cfg {
+  static constexpr int kABlocks = RB * U;                 // 1 KiB A fragments per batch
+  static constexpr int kACopiesPerWave = kABlocks / 4;    // spread over the 4 waves
+  static constexpr int kSCopies = U / 2;                  // 256-byte scale copies per wave per batch
+  static constexpr int kOpsPerBatch = kACopiesPerWave + kSCopies + U;
+  static constexpr int kABatchBytes = kABlocks * 1024;
+  static constexpr int kSBatchBytes = U * kScaleUnitElems * 2;
+  static constexpr int kLdsBytes = DEPTH * kABatchBytes + 4 * DEPTH * kSBatchBytes;
+  static_assert(kABlocks % 4 == 0 && U % 2 == 0, "batch shape");
+  static_assert(kOpsPerBatch * (DEPTH - 2) < 64, "vmcnt range");
+};
+
+// Issue batch b (groups b U .. b U + U - 1) into ring slot `slot`: this wave's
+// A fragment copies, its scale copies, then its nibble loads (in that order,
+// so a wait for the nibbles also covers the copies).
+template <int RB, int U, int DEPTH>
+__device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int b, int wave,
+                                            const uint8_t* const* a_src,
+                                            const uint8_t* ws, const uint8_t* wq, uint8_t* a_ring, uint8_t* s_ring) {
+  using C = Cfg<RB, U, DEPTH>;
+  int g0 = b * U;
+  asm volatile("" : "+s"(g0));  // keep the look-ahead where it is written
+#pragma unroll
+  for (int t = 0; t < C::kACopiesPerWave; ++t) {
+    const int j = wave + 4 * t;
+    __builtin_amdgcn_global_load_lds(a_src[t] + (int64_t)g0 * (kGroup * 2),
+                                     LDS_PTR(a_ring + slot * C::kABatchBytes + j * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < C::kSCopies; ++t)
+    __builtin_amdgcn_global_load_lds(ws + (int64_t)(g0 + 2 * t) * (kScaleUnitElems * 2),
+                                     LDS_PTR(s_ring + slot * C::kSBatchBytes + t * 256), 4, 0, kNonTemporal);
+#pragma unroll
+  for (int uu = 0; uu < U; ++uu)
+    nib[uu] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wq + (int64_t)(g0 + uu) * kNibUnitBytes));
+}
+
+template <int MODE, int RB, int U, int DEPTH>
+__global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p) {
+  using C = Cfg<RB, U, DEPTH>;
+  constexpr int BM = 16 * RB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = (int)threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  uint8_t* a_ring = lds;
+  uint8_t* s_ring = lds + DEPTH * C::kABatchBytes + wave * DEPTH * C::kSBatchBytes;
+
+  const int ntpp = min(*p.ntpp, p.capacity);
+  const int n_mblocks = ntpp / BM;
+  const int NB = p.N / kNBlock;
+  const int NG = NB / kUnitNBlocks;
+  const int G = p.K / kGroup;
+  const int nbatch = G / U;
+  const int units = n_mblocks * NG;
+  const int per_wg = (units + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int u_begin = (int)blockIdx.x * per_wg;
+  const int u_end = min(units, u_begin + per_wg);
+  uint32_t magic = kBf16_128;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
+  const bf16x8 minus136 = as_bf16x8(u32x4{kBf16_Minus136, kBf16_Minus136, kBf16_Minus136, kBf16_Minus136});
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int unit = u_begin; unit < u_end; ++unit) {
+    const int mb = unit / NG;
+    const int ng = unit - mb * NG;
+    const int e = p.expert_ids[mb];
+    if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
+    const int nb = ng * kUnitNBlocks + wave;
+
+    // A copy sources: this wave copies fragment blocks j = wave + 4 t of each
+    // batch, block j = (row block j / U, group j % U). Padding rows read the
+    // row block's first row; their results are never stored.
+    const uint8_t* a_src[C::kACopiesPerWave];
+#pragma unroll
+    for (int t = 0; t < C::kACopiesPerWave; ++t) {
+      const int j = wave + 4 * t;
+      const int rb = j / U, uu = j % U;
+      const int prow = mb * BM + rb * 16 + (lane & 15);
+      const int id = p.sorted[prow];
+      const bool real = (unsigned)id < (unsigned)p.n_slots;
+      int64_t src;
+      if (MODE == kGateUp) {
+        const int id0 = p.sorted[mb * BM];
+        src = (real ? id : id0) / p.topk;
+      } else {
+        src = real ? prow : mb * BM;
+      }
+      a_src[t] = reinterpret_cast<const uint8_t*>(p.a + src * p.K) + 16 * (lane >> 4) + uu * (kGroup * 2);
+    }
+    const int64_t unit0 = ((int64_t)e * NB + nb) * G;
+    const uint8_t* wq = p.wq + unit0 * kNibUnitBytes + 16 * lane;
+    const uint8_t* ws = reinterpret_cast<const uint8_t*>(p.ws + unit0 * kScaleUnitElems) + 4 * lane;
+
+    floatx4 acc[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[rb][c] = zero4;
+
+    u32x4 nib[DEPTH][U];
+    ring_barrier();  // the previous unit's reads of every slot are done
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s)
+      if (s < nbatch) issue_batch<RB, U, DEPTH>(nib[s], s, s, wave, a_src, ws, wq, a_ring, s_ring);
+
+    for (int b0 = 0; b0 < nbatch; b0 += DEPTH) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        const int b = b0 + k;
+        if (b < nbatch) {
+          if (b + DEPTH - 2 < nbatch) wait_vmcnt<C::kOpsPerBatch * (DEPTH - 2)>();
+          else wait_vmcnt<0>();
+          ring_barrier();
+          if (b + DEPTH - 1 < nbatch)
+            issue_batch<RB, U, DEPTH>(nib[(k + DEPTH - 1) % DEPTH], (k + DEPTH - 1) % DEPTH, b + DEPTH - 1, wave,
+                                      a_src, ws, wq, a_ring, s_ring);
+          const uint8_t* abase = a_ring + k * C::kABatchBytes;
+          const uint8_t* sbase = s_ring + k * C::kSBatchBytes;
+#pragma unroll
+          for (int uu = 0; uu < U; ++uu) {
+            const u32x2 sc = *reinterpret_cast<const u32x2*>(sbase + uu * 128 + 8 * (lane & 15));
+            const float scale[4] = {__uint_as_float(sc.x << 16), __uint_as_float(sc.x & 0xFFFF0000u),
+                                    __uint_as_float(sc.y << 16), __uint_as_float(sc.y & 0xFFFF0000u)};
+            bf16x8 w[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[c] = codes_to_bf16(nib[k][uu][c], magic);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (rb * U + uu) * 1024 + 16 * lane));
+              const floatx4 corr = mfma16(a, minus136, zero4);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc[rb][c] += scale[c] * mfma16(a, w[c], corr);
+            }
+          }
+        }
+      }
+    }
+
+    // Epilogue: element i of a 16x16 tile is row 4 (lane >> 4) + i, column lane & 15.
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int prow = mb * BM + rb * 16 + 4 * (lane >> 4) + i;
+        const int id = p.sorted[prow];
+        if ((unsigned)id >= (unsigned)p.n_slots) continue;
+        if (MODE == kGateUp) {
+          __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + (lane & 15);
+          h[0] = (__bf16)silu_mul(acc[rb][0][i], acc[rb][2][i]);
+          h[16] = (__bf16)silu_mul(acc[rb][1][i], acc[rb][3][i]);
+        } else {
+          float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + nb * kNBlock + (lane & 15);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[16 * c] = acc[rb][c][i];
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int RB, int U, int DEPTH>
+hipError_t launch(const GemmParams& p, hipStream_t stream) {
+  using C = Cfg<RB, U, DEPTH>;
+  constexpr int BM = 16 * RB;
+  const int64_t units_max = (int64_t)(p.capacity / BM) * (p.N / (kNBlock * kUnitNBlocks));
+  if (units_max == 0) return hipSuccess;
+  static int blocks_per_cu = [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>, kThreads,
+                                                     C::kLdsBytes) != hipSuccess ||
+        n < 1)
+      n = 1;
+    return n;
+  }();
+  const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu);
+  hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>), dim3((int)grid), dim3(kThreads), C::kLdsBytes,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(int32_t block_m, const GemmParams& p, hipStream_t stream) {
+  switch (block_m) {
+    case 16: return launch<MODE, 1, 4, 4>(p, stream);
+    case 32: return launch<MODE, 2, 4, 4>(p, stream);
+    case 64: return launch<MODE, 4, 4, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool stream_lds_supported(int32_t block_m, const GemmParams& p) {
+  return (block_m == 16 || block_m == 32 || block_m == 64) && p.N % (kNBlock * kUnitNBlocks) == 0 &&
+         (p.K / kGroup) % 4 == 0;
+}
+
+hipError_t launch_moe_gemm_stream_lds(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream) {
+  return mode == kGateUp ? launch_mode<kGateUp>(block_m, p, stream) : launch_mode<kDown>(block_m, p, stream);
+}
+
+}  // namespace w4a16

@@ -51,6 +51,9 @@ constexpr int kBBytes = kTileNBlocks * kStageGroups * kNibUnitBytes;         // 
 constexpr int kSBytes = kTileNBlocks * kStageGroups * kScaleUnitElems * 2;   // 1 KiB
 constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
 constexpr int kCopiesPerWaveStage = 4;  // 2 A blocks + 1 nibble unit + 1 scale unit
+// Weights and scales are read once per tile: copied with the non-temporal
+// policy (operand 2 = nt) so they do not evict the A tile shared through L2.
+constexpr int kNonTemporal = 2;
 
 constexpr uint32_t kCodeMask = 0x000F000Fu;
 constexpr uint32_t kBf16_128 = 0x43004300u;
@@ -118,7 +121,7 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int
   {
     const uint8_t* src = c.wq + (int64_t)(g0 + c.copy_j) * kNibUnitBytes + 16 * lane;
     __builtin_amdgcn_global_load_lds(src, LDS_PTR(base + kABytes + (c.copy_nb * kStageGroups + c.copy_j) * 1024), 16,
-                                     0, 0);
+                                     0, kNonTemporal);
   }
   // 128 bytes of scales: a dword copy lands at LDS base + 4 * lane, so only
   // lanes 0..31 take part (one instruction per wave either way, which keeps
@@ -126,7 +129,7 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int
   if (lane < 32) {
     const uint8_t* src = c.ws + (int64_t)(g0 + c.copy_j) * (kScaleUnitElems * 2) + 4 * lane;
     __builtin_amdgcn_global_load_lds(
-        src, LDS_PTR(base + kABytes + kBBytes + (c.copy_nb * kStageGroups + c.copy_j) * 128), 4, 0, 0);
+        src, LDS_PTR(base + kABytes + kBBytes + (c.copy_nb * kStageGroups + c.copy_j) * 128), 4, 0, kNonTemporal);
   }
 }
 
