@@ -46,7 +46,7 @@ def test_align_workloads(name):
         check(c.topk_ids, c.E, bm, what=name)
 
 
-@pytest.mark.parametrize("n_ids", [4095, 4096, 4097, 8192, 8193, 12289])
+@pytest.mark.parametrize("n_ids", [4096, 8191, 8192, 8193, 16384, 16385, 24577])
 def test_align_path_boundaries(n_ids):
     rng = np.random.default_rng(n_ids)
     ids = rng.integers(-3, 70, size=(n_ids, 1)).astype(np.int32)

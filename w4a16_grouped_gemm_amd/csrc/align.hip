@@ -10,29 +10,33 @@
 // "코드 분석"). Like that router, every counter is zeroed at kernel entry
 // (section "커널 내부 로직 변경 (추정)"), so no workspace needs clearing.
 //
-// Design:
-//  * histogram: LDS atomics on per-expert counters (counts are order-free, so
-//    the result is deterministic);
+// Design (the work is tiny; the kernels are written against latency):
+//  * every thread loads its ids once, up front, into registers;
+//  * histogram: LDS atomics on per-expert counters (order-free, so deterministic);
 //  * offsets: one wave scans the padded counts with lane shuffles;
-//  * ranking: a 1024-thread block walks its ids in rounds of 1024; inside a
-//    wave, lanes holding the same expert are found with one ballot per bit of
-//    the expert id, and a lane's rank is the mbcnt of its peers below it; the
-//    per-wave counts are prefix-summed across the 16 waves per expert in LDS.
-//    Positions therefore depend only on the input, never on timing.
-//  * small inputs (<= kSmallMax ids) run all phases in one block and one launch;
-//    larger ones split the ids over blocks: histogram kernel, one-block scan
-//    kernel, then a ranking/scatter kernel whose blocks start from the scanned
-//    per-block bases.
+//  * ranking: each wave owns a contiguous segment of ids and ranks it 64 at a
+//    time against its own per-expert counters in LDS (lanes of one expert are
+//    found with one ballot per bit of the expert id; a lane's rank is the
+//    mbcnt of its peers below it); one scan per expert across the 16 waves
+//    gives the bases. Positions depend only on the input, never on timing;
+//  * padding sentinels are written per expert (at most block_m - 1 each), used
+//    blocks are labelled with one search each, and the unused tail is a plain
+//    fill: no per-position search over the over-allocated buffer.
+// Small inputs run in one block and one launch. Larger ones use two launches:
+// per-chunk histograms, then one block per chunk that recomputes the (small)
+// expert prefix itself from all chunk histograms and scatters its chunk.
 #include "internal.h"
+
+#include <algorithm>
 
 namespace w4a16 {
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kSmallMax = 4096;  // ids handled by the single-launch path
-constexpr int kChunk = 4096;     // ids per block in the multi-block path
-
+constexpr int kPerThread = 8;                        // ids per thread held in registers
+constexpr int kChunk = kThreads * kPerThread;        // ids per block (8192)
+constexpr int kSmallMax = kChunk;                    // single-launch path up to here
 
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ int rank_below(uint64_t mask) {
@@ -41,12 +45,30 @@ __device__ __forceinline__ int rank_below(uint64_t mask) {
 
 __device__ __forceinline__ int padded(int c, int bm) { return (c + bm - 1) / bm * bm; }
 
-// Histogram of resident ids in [lo, hi) into LDS `hist` (zeroed by the caller).
-__device__ void count_ids(const int32_t* __restrict__ ids, int lo, int hi, int E, int* hist) {
-  for (int i = lo + (int)threadIdx.x; i < hi; i += kThreads) {
-    const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+__device__ __forceinline__ int id_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// Steps per wave for the ids [lo, hi) of one block: each of the 16 waves owns
+// a contiguous segment of 64 * steps ids and walks it 64 per step.
+__device__ __forceinline__ int block_steps(int lo, int hi) { return max(1, (hi - lo + kThreads - 1) / kThreads); }
+
+__device__ __forceinline__ int id_index(int lo, int steps, int r) {
+  return lo + ((int)threadIdx.x >> 6) * 64 * steps + 64 * r + ((int)threadIdx.x & 63);
+}
+
+// This lane's ids, one per step; -1 past `hi` and for unused steps.
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int lo, int hi, int steps,
+                                         int (&v)[kPerThread]) {
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const int i = id_index(lo, steps, r);
+    v[r] = (r < steps && i < hi) ? ids[i] : -1;
   }
+}
+
+__device__ __forceinline__ void count_ids(const int (&v)[kPerThread], int E, int* hist) {
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r)
+    if ((unsigned)v[r] < (unsigned)E) atomicAdd(&hist[v[r]], 1);
 }
 
 // Wave 0 writes off[0..E] = exclusive prefix of padded counts; off[E] = total.
@@ -62,8 +84,8 @@ __device__ void scan_offsets(const int* counts, int E, int bm, int* off) {
     }
     int incl = local;
     for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
+      const int x = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += x;
     }
     int run = incl - local;
     for (int k = 0; k < per; ++k) {
@@ -87,67 +109,75 @@ __device__ __forceinline__ int find_expert(const int* off, int E, int p) {
   return lo;
 }
 
-// expert_ids for blocks [b0, nblk) with stride `step`; -1 past the used blocks.
-__device__ void fill_expert_ids(const int* off, int E, int bm, int ntpp, int32_t* expert_ids, int nblk,
-                                int b0, int step) {
-  for (int b = b0; b < nblk; b += step) {
-    const int p = b * bm;
-    expert_ids[b] = (p < ntpp) ? find_expert(off, E, p) : -1;
-  }
+// Used blocks get their expert (one search per block, blocks strided from
+// t0); each expert's at most bm - 1 padding slots get the sentinel.
+__device__ void label_experts(const int* off, const int* counts, int E, int bm, int32_t* sorted,
+                              int32_t* expert_ids, int sentinel, int t0, int step) {
+  const int used = off[E] / bm;
+  for (int b = t0; b < used; b += step) expert_ids[b] = find_expert(off, E, b * bm);
+  for (int e = t0; e < E; e += step)
+    for (int p = off[e] + counts[e]; p < off[e + 1]; ++p) sorted[p] = sentinel;
 }
 
-// Sentinel for every padding position in [p0, capacity) with stride `step`:
-// positions past ntpp, and the tail of each expert's padded segment.
-__device__ void fill_padding(const int* off, const int* counts, int E, int ntpp, int32_t* sorted, int capacity,
-                             int sentinel, int p0, int step) {
-  for (int p = p0; p < capacity; p += step) {
-    if (p >= ntpp) {
-      sorted[p] = sentinel;
-    } else {
-      const int e = find_expert(off, E, p);
-      if (p - off[e] >= counts[e]) sorted[p] = sentinel;
-    }
-  }
+// Unused tail: sorted[ntpp, capacity) = sentinel, expert_ids[ntpp / bm, nblk) = -1.
+__device__ void fill_tail(int ntpp, int bm, int32_t* sorted, int capacity, int32_t* expert_ids, int nblk,
+                          int sentinel, int t0, int step) {
+  for (int p = ntpp + t0; p < capacity; p += step) sorted[p] = sentinel;
+  for (int b = ntpp / bm + t0; b < nblk; b += step) expert_ids[b] = -1;
 }
 
-// Stable scatter of the resident ids in [lo, hi): the id at flat index i goes
-// to cursor[e] + (resident ids of e in [lo, i)). cursor is advanced in place.
-// wtab is LDS scratch of kWaves * E ints.
-__device__ void scatter_ids(const int32_t* __restrict__ ids, int lo, int hi, int E, int nbits, int* cursor,
-                            int* wtab, int32_t* __restrict__ sorted) {
+// Stable scatter of the block's ids (held in v, see id_index): the id at flat
+// index i goes to cursor[e] + (resident ids of e before i in this block).
+// Each wave ranks its own contiguous segment step by step against a
+// wave-private counter row wcnt[wave][e] in LDS (lanes of one expert in a step
+// are found with one ballot per id bit; the rank is the mbcnt of the peers
+// below), so the steps need no workgroup barrier. The 16 per-wave counts of an
+// expert are then turned into per-wave bases by a 16-lane segmented shuffle
+// scan. wcnt is LDS scratch of kWaves * E ints.
+__device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nbits, const int* cursor, int* wcnt,
+                            int32_t* __restrict__ sorted, int lo) {
   const int wave = (int)threadIdx.x >> 6;
-  for (int base = lo; base < hi; base += kThreads) {
-    const int i = base + (int)threadIdx.x;
-    const int e = (i < hi) ? ids[i] : -1;
-    const bool local = (unsigned)e < (unsigned)E;
-    for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
-    // lanes of this wave holding the same expert: intersect one ballot per id bit
-    uint64_t peers = __ballot(local);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = __ballot(local && bit);
-      peers &= bit ? m : ~m;
-    }
-    const int rank = rank_below(peers);
-    __syncthreads();  // wtab cleared
-    if (local && rank == 0) wtab[wave * E + e] = __popcll(peers);
-    __syncthreads();  // per-wave counts visible
-    for (int x = (int)threadIdx.x; x < E; x += kThreads) {
-      int run = cursor[x];
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = wtab[w * E + x];
-        wtab[w * E + x] = run;
-        run += c;
+  int* row = wcnt + wave * E;
+  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wcnt[k] = 0;
+  __syncthreads();
+  int rank[kPerThread];
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    rank[r] = 0;
+    if (r < steps) {  // uniform
+      const int e = v[r];
+      const bool local = (unsigned)e < (unsigned)E;
+      uint64_t peers = __ballot(local);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(local && bit);
+        peers &= bit ? m : ~m;
       }
-      cursor[x] = run;
+      const int below = rank_below(peers);
+      const int prev = local ? row[e] : 0;  // every lane reads before the leader writes
+      rank[r] = prev + below;
+      if (local && below == 0) row[e] = prev + __popcll(peers);
     }
-    __syncthreads();  // per-wave bases visible
-    if (local) sorted[wtab[wave * E + e] + rank] = i;
-    __syncthreads();  // bases consumed before the next round clears wtab
   }
+  __syncthreads();  // all waves' counts final
+  // pair (expert x, wave w) at index 16 x + w: 16 consecutive lanes hold one expert
+  // kWaves * E is a multiple of 16, so every 16-lane segment is fully active
+  for (int idx = (int)threadIdx.x; idx < kWaves * E; idx += kThreads) {
+    const int x = idx >> 4, w = idx & 15;
+    const int c = wcnt[w * E + x];
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < kWaves; d <<= 1) {
+      const int up = __shfl_up(incl, d, kWaves);
+      if (w >= d) incl += up;
+    }
+    wcnt[w * E + x] = cursor[x] + incl - c;  // only this lane ever touches this entry
+  }
+  __syncthreads();  // per-wave bases visible
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r)
+    if (r < steps && (unsigned)v[r] < (unsigned)E) sorted[row[v[r]] + rank[r]] = id_index(lo, steps, r);
 }
-
-__device__ __forceinline__ int id_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
 
 // ---- single-launch path -----------------------------------------------------
 // LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
@@ -161,9 +191,12 @@ __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __
   int* off = counts + E;
   int* cursor = off + E + 1;
   int* wtab = cursor + E;
+  int v[kPerThread];
+  const int steps = block_steps(0, n);
+  load_ids(ids, 0, n, steps, v);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = 0;
   __syncthreads();
-  count_ids(ids, 0, n, E, counts);
+  count_ids(v, E, counts);
   __syncthreads();
   scan_offsets(counts, E, bm, off);
   __syncthreads();
@@ -173,80 +206,76 @@ __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __
     cursor[e] = off[e];
     if (counts_out) counts_out[e] = counts[e];
   }
-  fill_expert_ids(off, E, bm, ntpp, expert_ids, nblk, (int)threadIdx.x, kThreads);
-  fill_padding(off, counts, E, ntpp, sorted, capacity, n, (int)threadIdx.x, kThreads);
+  label_experts(off, counts, E, bm, sorted, expert_ids, n, (int)threadIdx.x, kThreads);
+  fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, (int)threadIdx.x, kThreads);
   __syncthreads();
-  scatter_ids(ids, 0, n, E, id_bits(E), cursor, wtab, sorted);
+  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, 0);
 }
 
 // ---- multi-block path -------------------------------------------------------
-// Workspace: hist[nchunks * E] (per-chunk counts, then per-chunk bases),
-// off[E + 1], counts[E].
-
+// Workspace: hist[nchunks * E], the per-chunk resident counts.
 __global__ __launch_bounds__(kThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                               int* __restrict__ hist) {
   extern __shared__ int smem[];
+  int v[kPerThread];
+  const int lo = (int)blockIdx.x * kChunk;
+  load_ids(ids, lo, min(n, lo + kChunk), block_steps(lo, min(n, lo + kChunk)), v);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) smem[e] = 0;
   __syncthreads();
-  const int lo = (int)blockIdx.x * kChunk;
-  count_ids(ids, lo, min(n, lo + kChunk), E, smem);
+  count_ids(v, E, smem);
   __syncthreads();
   for (int e = (int)threadIdx.x; e < E; e += kThreads) hist[(size_t)blockIdx.x * E + e] = smem[e];
 }
 
-__global__ __launch_bounds__(kThreads) void align_scan_kernel(int* __restrict__ hist, int nchunks, int E, int bm,
-                                                              int* __restrict__ off_out, int* __restrict__ counts_ws,
-                                                              int32_t* __restrict__ expert_ids, int nblk,
-                                                              int32_t* __restrict__ ntpp_out,
-                                                              int32_t* __restrict__ counts_out) {
+// One block per chunk. Every block reads all chunk histograms (nchunks * E
+// entries) to get the expert totals, the offsets and its own chunk's base;
+// block 0 also writes the counts, the padded total and the block labels; all
+// blocks share the sentinel fill of the tail.
+// LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
+__global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
+                                                                 const int* __restrict__ hist, int nchunks,
+                                                                 int32_t* __restrict__ sorted, int capacity,
+                                                                 int32_t* __restrict__ expert_ids, int nblk,
+                                                                 int32_t* __restrict__ ntpp_out,
+                                                                 int32_t* __restrict__ counts_out) {
   extern __shared__ int smem[];
   int* counts = smem;
   int* off = counts + E;
+  int* cursor = off + E + 1;
+  int* wtab = cursor + E;
+  int v[kPerThread];
+  const int lo = (int)blockIdx.x * kChunk;
+  const int steps = block_steps(lo, min(n, lo + kChunk));
+  load_ids(ids, lo, min(n, lo + kChunk), steps, v);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) {
-    int run = 0;
+    int total = 0, before = 0;
+#pragma unroll 8  // independent loads in flight (the histograms sit in L2)
     for (int b = 0; b < nchunks; ++b) {
       const int c = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;  // exclusive prefix over chunks (relative to off[e])
-      run += c;
+      before += (b < (int)blockIdx.x) ? c : 0;
+      total += c;
     }
-    counts[e] = run;
+    counts[e] = total;
+    cursor[e] = before;  // this chunk's base inside the expert, before adding off[e]
   }
   __syncthreads();
   scan_offsets(counts, E, bm, off);
   __syncthreads();
   const int ntpp = off[E];
-  if (threadIdx.x == 0) *ntpp_out = ntpp;
-  for (int e = (int)threadIdx.x; e <= E; e += kThreads) off_out[e] = off[e];
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
-    counts_ws[e] = counts[e];
-    if (counts_out) counts_out[e] = counts[e];
+  for (int e = (int)threadIdx.x; e < E; e += kThreads) cursor[e] += off[e];
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) *ntpp_out = ntpp;
+    for (int e = (int)threadIdx.x; e < E; e += kThreads)
+      if (counts_out) counts_out[e] = counts[e];
   }
-  fill_expert_ids(off, E, bm, ntpp, expert_ids, nblk, (int)threadIdx.x, kThreads);
+  const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
+  label_experts(off, counts, E, bm, sorted, expert_ids, n, gt, gstep);
+  fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, gt, gstep);
+  __syncthreads();
+  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, lo);
 }
 
-// LDS: off[E+1], counts[E], cursor[E], wtab[kWaves*E]
-__global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                                 const int* __restrict__ hist,
-                                                                 const int* __restrict__ off_ws,
-                                                                 const int* __restrict__ counts_ws,
-                                                                 int32_t* __restrict__ sorted, int capacity) {
-  extern __shared__ int smem[];
-  int* off = smem;
-  int* counts = off + E + 1;
-  int* cursor = counts + E;
-  int* wtab = cursor + E;
-  for (int e = (int)threadIdx.x; e <= E; e += kThreads) off[e] = off_ws[e];
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = counts_ws[e];
-  __syncthreads();
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) cursor[e] = off[e] + hist[(size_t)blockIdx.x * E + e];
-  fill_padding(off, counts, E, off[E], sorted, capacity, n, (int)(blockIdx.x * kThreads + threadIdx.x),
-               (int)(gridDim.x * kThreads));
-  __syncthreads();
-  const int lo = (int)blockIdx.x * kChunk;
-  scatter_ids(ids, lo, min(n, lo + kChunk), E, id_bits(E), cursor, wtab, sorted);
-}
-
-// T == 0 or nothing to rank: every output is a sentinel.
+// T == 0: every output is a sentinel.
 __global__ void align_empty_kernel(int32_t* sorted, int capacity, int sentinel, int32_t* expert_ids, int nblk,
                                    int32_t* ntpp_out, int32_t* counts_out, int E) {
   const int tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
@@ -259,12 +288,14 @@ __global__ void align_empty_kernel(int32_t* sorted, int capacity, int sentinel, 
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+size_t scatter_lds(int E) { return sizeof(int) * (size_t)(3 * E + 1 + kWaves * E); }
+
 }  // namespace
 
 size_t align_workspace_bytes(int64_t n, int32_t E) {
   if (n <= kSmallMax) return 0;
   const int64_t nchunks = (n + kChunk - 1) / kChunk;
-  return round_up(sizeof(int) * (size_t)(nchunks * E + 2 * E + 1), 256);
+  return round_up(sizeof(int) * (size_t)(nchunks * E), 256);
 }
 
 hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, int32_t* sorted, int32_t capacity,
@@ -277,26 +308,18 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, in
     return hipGetLastError();
   }
   if (n <= kSmallMax) {
-    const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + kWaves * E);
-    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kThreads), lds, stream, ids, n, E, bm, sorted, capacity,
-                       expert_ids, nblk, ntpp, counts);
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, sorted,
+                       capacity, expert_ids, nblk, ntpp, counts);
     return hipGetLastError();
   }
   const int nchunks = (n + kChunk - 1) / kChunk;
   int* hist = static_cast<int*>(workspace);
-  int* off = hist + (size_t)nchunks * E;
-  int* counts_ws = off + E + 1;
   hipLaunchKernelGGL(align_hist_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, stream, ids, n, E,
                      hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kThreads), sizeof(int) * (size_t)(2 * E + 1), stream, hist,
-                     nchunks, E, bm, off, counts_ws, expert_ids, nblk, ntpp, counts);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + kWaves * E);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kThreads), lds, stream, ids, n, E, hist, off,
-                     counts_ws, sorted, capacity);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, hist,
+                     nchunks, sorted, capacity, expert_ids, nblk, ntpp, counts);
   return hipGetLastError();
 }
 

@@ -241,29 +241,36 @@ __global__ __launch_bounds__(256) void moe_gemm_stream_kernel(GemmParams p) {
 }
 
 // out[t, n] = bf16(sum_j resident(t, j) * w[t, j] * y[t*topk + j, n]), fp32 in j order.
+// One 256-thread block per (token, `cols` columns); each thread owns 8
+// consecutive columns at a time (two 16-byte reads per resident slot, one
+// 16-byte store). Tokens with no resident slot only write zeros.
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
                                                       const float* __restrict__ y, uint16_t* __restrict__ out, int topk,
-                                                      int H, int E) {
-  const int chunks = (H / 4 + 255) / 256;
+                                                      int H, int E, int cols) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int chunks = (H + cols - 1) / cols;
   const int t = (int)blockIdx.x / chunks;
-  const int n0 = (((int)blockIdx.x - t * chunks) * 256 + (int)threadIdx.x) * 4;
-  if (n0 >= H) return;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int slot = t * topk + j;
-    const int e = ids[slot];
-    if ((unsigned)e >= (unsigned)E) continue;
-    const float wt = w[slot];
-    const floatx4 v = *reinterpret_cast<const floatx4*>(y + (int64_t)slot * H + n0);
-    acc += wt * v;
+  const int c0 = ((int)blockIdx.x - t * chunks) * cols;
+  const int c1 = min(H, c0 + cols);
+  for (int n0 = c0 + 8 * (int)threadIdx.x; n0 < c1; n0 += 8 * 256) {
+    floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < topk; ++j) {
+      const int slot = t * topk + j;
+      const int e = ids[slot];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const float wt = w[slot];
+      const floatx4* src = reinterpret_cast<const floatx4*>(y + (int64_t)slot * H + n0);
+      lo += wt * src[0];
+      hi += wt * src[1];
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = (__bf16)lo[i];
+      r[4 + i] = (__bf16)hi[i];
+    }
+    *reinterpret_cast<bf16x8*>(out + (int64_t)t * H + n0) = r;
   }
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 r;
-  r[0] = (__bf16)acc[0];
-  r[1] = (__bf16)acc[1];
-  r[2] = (__bf16)acc[2];
-  r[3] = (__bf16)acc[3];
-  *reinterpret_cast<bf16x4*>(out + (int64_t)t * H + n0) = r;
 }
 
 std::atomic<int> g_cu_count[64];
@@ -320,8 +327,10 @@ hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, 
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* y, uint16_t* out, int32_t T, int32_t topk,
                           int32_t H, int32_t E, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int chunks = (H / 4 + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3(T * chunks), dim3(256), 0, stream, ids, w, y, out, topk, H, E);
+  // few tokens: split rows over blocks for parallelism; many tokens: a block per row
+  const int cols = T >= 256 ? H : 8 * 256;
+  const int64_t blocks = (int64_t)T * ((H + cols - 1) / cols);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ids, w, y, out, topk, H, E, cols);
   return hipGetLastError();
 }
 

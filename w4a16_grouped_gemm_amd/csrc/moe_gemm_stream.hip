@@ -257,7 +257,11 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
       n = 1;
     return n;
   }();
-  const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu);
+  // Up to 4x the resident workgroups: when the live units outnumber the
+  // resident slots, queued workgroups start as others finish, instead of a
+  // resident workgroup restarting its pipeline for a second unit (measured
+  // faster for the decode down projection).
+  const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu * 4);
   hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>), dim3((int)grid), dim3(kThreads), C::kLdsBytes,
                      stream, p);
   return hipGetLastError();
@@ -266,7 +270,7 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
 template <int MODE>
 hipError_t launch_mode(int32_t block_m, const GemmParams& p, hipStream_t stream) {
   switch (block_m) {
-    case 16: return launch<MODE, 1, 4, 4>(p, stream);
+    case 16: return launch<MODE, 1, 4, 3>(p, stream);
     case 32: return launch<MODE, 2, 4, 4>(p, stream);
     case 64: return launch<MODE, 4, 4, 3>(p, stream);
     default: return hipErrorInvalidValue;
