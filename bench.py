@@ -156,6 +156,7 @@ def main():
     h = ws[: ((cap * I * 2 + 255) // 256) * 256].view(torch.int16)[: cap * I].view(cap, I)
     y_off = ((cap * I * 2 + 255) // 256) * 256
     y = ws[y_off: y_off + T * topk * H * 4].view(torch.float32).view(T * topk, H)
+    scratch = ws[y_off + ((T * topk * H * 4 + 255) // 256) * 256:]
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     flush_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")  # 1 GiB, read to evict caches
 
@@ -170,11 +171,11 @@ def main():
         ev[0].record()
         align()
         ev[1].record()
-        w.w4a16_moe_gate_up(shape, x, T, topk, buf["sorted_token_ids"], buf["expert_ids"],
-                            buf["num_tokens_post_padded"], bm, w13p, h)
+        w.w4a16_moe_gate_up(shape, x, ids, buf["sorted_token_ids"], buf["expert_ids"],
+                            buf["num_tokens_post_padded"], bm, w13p, h, scratch)
         ev[2].record()
         w.w4a16_moe_down(shape, T, topk, h, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"],
-                         bm, w2p, y)
+                         bm, w2p, y, scratch)
         ev[3].record()
         w.w4a16_moe_combine(shape, ids, wts, y, out)
         ev[4].record()

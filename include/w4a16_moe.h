@@ -70,8 +70,10 @@ const char* w4a16_status_string(int status);
 /* Load time: weight repack                                                  */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of the two packed weight buffers written by w4a16_repack. They equal
- * the canonical sizes (nibbles + scales), rearranged. */
+/* Bytes of the two packed weight buffers written by w4a16_repack: the canonical
+ * nibbles and bf16 scales rearranged, plus a second copy of the scales in fp16
+ * normalised by a power of two per output channel and the channel exponents
+ * (read by the many-tokens-per-expert GEMM), about 1.13x the canonical size. */
 int w4a16_packed_bytes(const w4a16_moe_shape* shape, size_t* w13_bytes, size_t* w2_bytes);
 
 /* Rearrange canonical weights into the kernels' layout, once, before inference
@@ -140,8 +142,16 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
 /* ------------------------------------------------------------------------ */
 
 /* Device scratch bytes of w4a16_moe_forward: the bf16 SiLU-and-mul output
- * h [capacity, I] and the fp32 per-slot down outputs y [T*topk, H]. */
+ * h [capacity, I], the fp32 per-slot down outputs y [T*topk, H], and the
+ * scratch of the two GEMM stages (w4a16_moe_stage_workspace_bytes). */
 size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m);
+
+/* Device scratch bytes of w4a16_moe_gate_up and w4a16_moe_down (one region,
+ * usable by both since they run one after the other): with block_m = 128 the
+ * GEMMs first convert the activation rows they read to fp16 with a
+ * power-of-two factor per row (T rows of x, then moe_align_capacity rows of h);
+ * 0 for the other block_m values. */
+size_t w4a16_moe_stage_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m);
 
 /* out[t, :] = bf16( sum_j [0 <= topk_ids[t,j] < E] * topk_weights[t,j] *
  *                    W2[e] . bf16(silu(W13_gate[e] . x[t]) * (W13_up[e] . x[t])) )
@@ -169,7 +179,9 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
                       void* stream);
 
 /* The three stages of w4a16_moe_forward, callable one by one (same arguments
- * and conventions; forward == gate_up, then down, then combine).
+ * and conventions; forward == gate_up, then down, then combine). gate_up and
+ * down take a scratch region of w4a16_moe_stage_workspace_bytes (may be NULL
+ * when that is 0), rewritten by each call.
  *
  * gate_up: h[p, c] = bf16(silu(g[p, c]) * g[p, I + c]) for every real row p of
  *   the aligned order (sorted_token_ids[p] < T*topk), g = x[sorted[p]/topk] . W13^T.
@@ -179,13 +191,14 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
  * combine: out[t, n] = bf16(sum_j resident(t, j) * topk_weights[t, j] * y[t*topk+j, n]),
  *   summed in fp32 in j order. */
 int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
-                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
-                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed,
-                      uint16_t* h, void* stream);
+                      const int32_t* topk_ids, const int32_t* sorted_token_ids, int32_t capacity,
+                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int32_t block_m,
+                      const void* w13_packed, uint16_t* h, void* workspace, size_t workspace_bytes,
+                      void* stream);
 int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
                    const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
                    const int32_t* num_tokens_post_padded, int32_t block_m, const void* w2_packed,
-                   float* y, void* stream);
+                   float* y, void* workspace, size_t workspace_bytes, void* stream);
 int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const int32_t* topk_ids,
                       const float* topk_weights, const float* y, uint16_t* out, void* stream);
 

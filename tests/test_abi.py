@@ -52,10 +52,16 @@ def test_sizes_and_heuristic(lib):
     assert w.moe_align_workspace_bytes(16384, 8, 48, 128) > 0
     s = w.make_shape(48, 7168, 2048)
     q13, q2 = w.w4a16_packed_bytes(s)
-    assert q13 == 48 * 4096 * 7168 // 2 + 48 * 4096 * 224 * 2
-    assert q2 == 48 * 7168 * 2048 // 2 + 48 * 7168 * 64 * 2
+    # nibbles, bf16 scales, fp16 scales, int32 channel exponents (all sizes here are 256-byte multiples)
+    assert q13 == 48 * 4096 * 7168 // 2 + 2 * 48 * 4096 * 224 * 2 + 48 * 4096 * 4
+    assert q2 == 48 * 7168 * 2048 // 2 + 2 * 48 * 7168 * 64 * 2 + 48 * 7168 * 4
     cap = w.moe_align_capacity(128, 8, 48, 16)
     assert w.w4a16_moe_workspace_bytes(s, 128, 8, 16) >= cap * 2048 * 2 + 128 * 8 * 7168 * 4
+    # block_m 128: plus fp16 copies of the x rows or of the aligned h rows, with a row exponent each
+    cap = w.moe_align_capacity(768, 8, 48, 128)
+    stage = w.w4a16_moe_stage_workspace_bytes(s, 768, 8, 128)
+    assert stage >= max(768 * 7168 * 2 + 768 * 4, cap * 2048 * 2 + cap * 4)
+    assert w.w4a16_moe_workspace_bytes(s, 768, 8, 128) >= cap * 2048 * 2 + 768 * 8 * 7168 * 4 + stage
     # tokens per expert drives the row-block size
     assert w.w4a16_choose_block_m(128, 8, 48, 384) == 16
     assert w.w4a16_choose_block_m(512, 8, 384, 384) == 32
@@ -99,8 +105,21 @@ def test_validation_status_codes(lib):
     # repack and stages
     assert lib.w4a16_repack(ctypes.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
-    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, 3, FAKE, FAKE, 16, FAKE, FAKE, None) == 3
-    assert lib.w4a16_moe_down(ctypes.byref(good), 4, 2, None, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None) == 1
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, FAKE, 3, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
+                                 None) == 3
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, None, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
+                                 None) == 1
+    assert lib.w4a16_moe_down(ctypes.byref(good), 4, 2, None, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
+                              None) == 1
+    # block_m 128 needs the stages' scratch
+    assert w.w4a16_moe_stage_workspace_bytes(good, 4, 2, 16) == 0
+    need = w.w4a16_moe_stage_workspace_bytes(good, 4, 2, 128)
+    assert need > 0
+    cap = w.moe_align_capacity(4, 2, 8, 128)
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, FAKE, cap, FAKE, FAKE, 128, FAKE, FAKE, None,
+                                 0, None) == 4
+    assert lib.w4a16_moe_down(ctypes.byref(good), 4, 2, FAKE, FAKE, cap, FAKE, FAKE, 128, FAKE, FAKE, FAKE, need - 1,
+                              None) == 4
 
 
 def test_binding_raises(lib):

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synthetic
-from _gpu import DeviceCase, parity, say, to_dev
+from _gpu import DeviceCase, bf16_to_f64, parity, say, to_dev
 
 import w4a16_grouped_gemm_amd as w
 
@@ -48,6 +48,44 @@ def test_small_cases(name, T, H, I, E, topk, Eg, bm):
     parity(d.forward(bm), oracle_rows(c), name)
 
 
+def test_wide_dynamic_range_block_m_128():
+    """Operands outside the fp16 range: activation rows of N(0,1) * 2^(r - 20)
+    for r in -24..8 (down to 2^-44, far below fp16's smallest subnormal), gate_up
+    scales near 2^13 (q * s beyond 65504), SiLU-and-mul outputs beyond 65504 in
+    the largest rows, one gate channel whose scales span 2^20 and one row with an
+    element 2^40 below its largest (both round on the fp16 subnormal grid after
+    normalisation). Output rows then span 2^-60..2^8.
+
+    Both block sizes meet the usual bound against the oracle. The bound's floor
+    of 1 hides errors in the tiny rows, so the fp16-operand path (block_m 128)
+    is also held to the bf16 streaming path (block_m 16, no fp16 anywhere) with
+    the floor taken per row: |y128 - y16| <= 2e-2 * max(rowmax / 32, |y16|) (a
+    normalisation slip would be off by O(rowmax))."""
+    c = synthetic.random_case("range", T=200, H=384, I=128, E=4, topk=2, block_m=128, seed=21)
+    x = synthetic.bf16_bits_to_f32(c.x).astype(np.float64)
+    r = (np.arange(c.T) % 9) * 4 - 24
+    x = x * np.exp2(r - 20.0)[:, None]
+    x[33, 5] = np.exp2(-20.0 - 40.0 + float(r[33]))  # 2^40 below its row
+    c.x = synthetic.to_bf16_bits(x.astype(np.float32))
+    s13 = synthetic.bf16_bits_to_f32(c.w13_s).astype(np.float64) * 2.0 ** 20
+    G = c.H // 32
+    s13[:, 3, :] = 2.0 ** (13 - np.linspace(0, 20, G))
+    c.w13_s = synthetic.to_bf16_bits(s13.astype(np.float32))
+    c.w2_s = synthetic.to_bf16_bits(synthetic.bf16_bits_to_f32(c.w2_s) * np.float32(2.0 ** -10))
+    say("layer wide dynamic range bm128")
+    d = DeviceCase(c)
+    ref = oracle_rows(c)
+    y128, y16 = d.forward(128), d.forward(16)
+    parity(y128, ref, "wide range bm128")
+    parity(y16, ref, "wide range bm16")
+    a, b = bf16_to_f64(y128), bf16_to_f64(y16)
+    floor = np.abs(b).max(axis=1, keepdims=True) / 32
+    assert floor.max() > 1.0 and floor[floor > 0].min() < 1e-15
+    err, tol = np.abs(a - b), 2e-2 * np.maximum(floor, np.abs(b))
+    say(f"  wide range bm128 vs bm16, per-row floor: max err/tol {(err / np.maximum(tol, 1e-300)).max():.4f}")
+    assert np.all(err <= tol), f"{(err > tol).sum()} elements differ beyond the per-row bound"
+
+
 def test_tokens_without_resident_expert_are_zero():
     c = synthetic.random_case("holes", T=50, H=256, I=64, E=6, topk=3, block_m=16, seed=7, E_global=30)
     ids = c.topk_ids.copy()
@@ -70,7 +108,7 @@ def test_stages_equal_forward_and_deterministic():
     h = torch.zeros((cap, c.I), dtype=torch.int16, device="cuda")
     y = torch.zeros((c.T * c.topk, c.H), dtype=torch.float32, device="cuda")
     out = torch.full((c.T, c.H), -1, dtype=torch.int16, device="cuda")
-    w.w4a16_moe_gate_up(d.shape, d.x, c.T, c.topk, buf["sorted_token_ids"], buf["expert_ids"],
+    w.w4a16_moe_gate_up(d.shape, d.x, d.ids, buf["sorted_token_ids"], buf["expert_ids"],
                         buf["num_tokens_post_padded"], 32, d.w13p, h)
     w.w4a16_moe_down(d.shape, c.T, c.topk, h, buf["sorted_token_ids"], buf["expert_ids"],
                      buf["num_tokens_post_padded"], 32, d.w2p, y)

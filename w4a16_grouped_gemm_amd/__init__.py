@@ -99,18 +99,28 @@ def w4a16_moe_forward(shape: Shape, x, topk_ids, topk_weights, sorted_token_ids,
                                     _p(workspace), nbytes, _stream(stream)), "w4a16_moe_forward")
 
 
-def w4a16_moe_gate_up(shape: Shape, x, T: int, topk: int, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                      block_m: int, w13_packed, h, stream=None):
-    _check(load().w4a16_moe_gate_up(ctypes.byref(shape), _p(x), T, topk, _p(sorted_token_ids),
+def w4a16_moe_stage_workspace_bytes(shape: Shape, T: int, topk: int, block_m: int) -> int:
+    return load().w4a16_moe_stage_workspace_bytes(ctypes.byref(shape), T, topk, block_m)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def w4a16_moe_gate_up(shape: Shape, x, topk_ids, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                      block_m: int, w13_packed, h, workspace=None, stream=None):
+    T, topk = topk_ids.shape
+    _check(load().w4a16_moe_gate_up(ctypes.byref(shape), _p(x), T, topk, _p(topk_ids), _p(sorted_token_ids),
                                     sorted_token_ids.numel(), _p(expert_ids), _p(num_tokens_post_padded), block_m,
-                                    _p(w13_packed), _p(h), _stream(stream)), "w4a16_moe_gate_up")
+                                    _p(w13_packed), _p(h), _p(workspace), _nbytes(workspace), _stream(stream)),
+           "w4a16_moe_gate_up")
 
 
 def w4a16_moe_down(shape: Shape, T: int, topk: int, h, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                   block_m: int, w2_packed, y, stream=None):
+                   block_m: int, w2_packed, y, workspace=None, stream=None):
     _check(load().w4a16_moe_down(ctypes.byref(shape), T, topk, _p(h), _p(sorted_token_ids), sorted_token_ids.numel(),
                                  _p(expert_ids), _p(num_tokens_post_padded), block_m, _p(w2_packed), _p(y),
-                                 _stream(stream)), "w4a16_moe_down")
+                                 _p(workspace), _nbytes(workspace), _stream(stream)), "w4a16_moe_down")
 
 
 def w4a16_moe_combine(shape: Shape, topk_ids, topk_weights, y, out, stream=None):

@@ -5,6 +5,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 using namespace w4a16;
@@ -41,8 +43,16 @@ int check_tokens(int32_t T, int32_t topk, int32_t E, int32_t block_m) {
 int hip_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
 GemmParams gemm_params(const w4a16_moe_shape* s, int32_t T, int32_t topk, const int32_t* sorted, int32_t capacity,
-                       const int32_t* expert_ids, const int32_t* ntpp) {
+                       const int32_t* expert_ids, const int32_t* ntpp, const void* packed, int32_t N, int32_t K) {
   GemmParams p{};
+  const PackedRegions r = packed_regions((size_t)s->num_experts, (size_t)N, (size_t)K);
+  const uint8_t* base = static_cast<const uint8_t*>(packed);
+  p.wq = base + r.nib;
+  p.ws = reinterpret_cast<const uint16_t*>(base + r.s_bf16);
+  p.ws16 = reinterpret_cast<const uint16_t*>(base + r.s_f16);
+  p.col_exp = reinterpret_cast<const int32_t*>(base + r.cexp);
+  p.N = N;
+  p.K = K;
   p.sorted = sorted;
   p.expert_ids = expert_ids;
   p.ntpp = ntpp;
@@ -74,9 +84,8 @@ int w4a16_packed_bytes(const w4a16_moe_shape* shape, size_t* w13_bytes, size_t* 
   if (st != W4A16_OK) return st;
   if (!w13_bytes || !w2_bytes) return W4A16_ERR_INVALID_ARG;
   const size_t E = (size_t)shape->num_experts, H = (size_t)shape->hidden, I = (size_t)shape->intermediate;
-  // nibbles + scales, each region 256-byte aligned
-  *w13_bytes = round_up(E * 2 * I * H / 2) + round_up(E * 2 * I * (H / 32) * 2);
-  *w2_bytes = round_up(E * H * I / 2) + round_up(E * H * (I / 32) * 2);
+  *w13_bytes = packed_regions(E, 2 * I, H).total;
+  *w2_bytes = packed_regions(E, H, I).total;
   return W4A16_OK;
 }
 
@@ -87,12 +96,9 @@ int w4a16_repack(const w4a16_moe_shape* shape, const uint8_t* w13_q, const uint1
   if (!w13_q || !w13_s || !w2_q || !w2_s || !w13_packed || !w2_packed) return W4A16_ERR_INVALID_ARG;
   const int32_t E = shape->num_experts, H = shape->hidden, I = shape->intermediate;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* p13 = static_cast<uint8_t*>(w13_packed);
-  uint8_t* p2 = static_cast<uint8_t*>(w2_packed);
-  const size_t q13 = round_up((size_t)E * 2 * I * H / 2), q2 = round_up((size_t)E * H * I / 2);
-  hipError_t e = launch_repack(w13_q, w13_s, E, 2 * I, H, I, p13, reinterpret_cast<uint16_t*>(p13 + q13), s);
+  hipError_t e = launch_repack(w13_q, w13_s, E, 2 * I, H, I, static_cast<uint8_t*>(w13_packed), s);
   if (e != hipSuccess) return W4A16_ERR_HIP;
-  e = launch_repack(w2_q, w2_s, E, H, I, 0, p2, reinterpret_cast<uint16_t*>(p2 + q2), s);
+  e = launch_repack(w2_q, w2_s, E, H, I, 0, static_cast<uint8_t*>(w2_packed), s);
   return hip_status(e);
 }
 
@@ -133,41 +139,53 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
                                  num_tokens_post_padded, expert_counts, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t w4a16_moe_stage_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m) {
+  if (check_shape(shape) != W4A16_OK) return 0;
+  if (check_tokens(T, topk, shape->num_experts, block_m) != W4A16_OK) return 0;
+  if (block_m != 128) return 0;
+  // the tiled path's fp16 A rows: x rows for gate_up, aligned h rows for down
+  // (the two stages run one after the other and share the region)
+  const size_t cap = moe_align_capacity(T, topk, shape->num_experts, block_m);
+  return round_up(std::max(tiled_scratch_bytes(T, shape->hidden), tiled_scratch_bytes((int64_t)cap, shape->intermediate)));
+}
+
 size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m) {
   if (check_shape(shape) != W4A16_OK) return 0;
   if (check_tokens(T, topk, shape->num_experts, block_m) != W4A16_OK) return 0;
   const size_t cap = moe_align_capacity(T, topk, shape->num_experts, block_m);
-  return round_up(cap * (size_t)shape->intermediate * 2) + round_up((size_t)T * topk * shape->hidden * 4);
+  return round_up(cap * (size_t)shape->intermediate * 2) + round_up((size_t)T * topk * shape->hidden * 4) +
+         w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
 }
 
 int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
-                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
-                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed, uint16_t* h,
-                      void* stream) {
+                      const int32_t* topk_ids, const int32_t* sorted_token_ids, int32_t capacity,
+                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int32_t block_m,
+                      const void* w13_packed, uint16_t* h, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != W4A16_OK) return st;
   st = check_tokens(T, topk, shape->num_experts, block_m);
   if (st != W4A16_OK) return st;
-  if ((T > 0 && !x) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w13_packed || !h)
+  if ((T > 0 && (!x || !topk_ids)) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w13_packed ||
+      !h)
     return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
-  const int32_t E = shape->num_experts, H = shape->hidden, I = shape->intermediate;
-  GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded);
+  const size_t need = w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
+  const int32_t H = shape->hidden, I = shape->intermediate;
+  GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded,
+                             w13_packed, 2 * I, H);
   p.a = x;
-  p.wq = static_cast<const uint8_t*>(w13_packed);
-  p.ws = reinterpret_cast<const uint16_t*>(p.wq + round_up((size_t)E * 2 * I * H / 2));
+  p.topk_ids = topk_ids;
   p.out = h;
-  p.K = H;
-  p.N = 2 * I;
   p.out_ld = I;
-  return hip_status(launch_moe_gemm(kGateUp, block_m, p, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_moe_gemm(kGateUp, block_m, p, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
                    const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
                    const int32_t* num_tokens_post_padded, int32_t block_m, const void* w2_packed, float* y,
-                   void* stream) {
+                   void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != W4A16_OK) return st;
   st = check_tokens(T, topk, shape->num_experts, block_m);
@@ -176,16 +194,19 @@ int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const 
     return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
-  const int32_t E = shape->num_experts, H = shape->hidden, I = shape->intermediate;
-  GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded);
+  // the tiled path converts rows [0, capacity) of h; the scratch is sized for
+  // moe_align_capacity rows, so a larger capacity is clamped to it (rows past
+  // it are never live: num_tokens_post_padded <= moe_align_capacity)
+  const size_t cap_min = moe_align_capacity(T, topk, shape->num_experts, block_m);
+  const size_t need = w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
+  const int32_t H = shape->hidden, I = shape->intermediate;
+  GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
+                             w2_packed, H, I);
   p.a = h;
-  p.wq = static_cast<const uint8_t*>(w2_packed);
-  p.ws = reinterpret_cast<const uint16_t*>(p.wq + round_up((size_t)E * H * I / 2));
   p.out = y;
-  p.K = I;
-  p.N = H;
   p.out_ld = H;
-  return hip_status(launch_moe_gemm(kDown, block_m, p, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_moe_gemm(kDown, block_m, p, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const int32_t* topk_ids,
@@ -217,16 +238,21 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
   const size_t need = w4a16_moe_workspace_bytes(shape, T, topk, block_m);
   if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
   if (T == 0) return W4A16_OK;
-  // workspace: h [cap_min, I] bf16, then y [T*topk, H] fp32
+  // workspace: h [cap_min, I] bf16, then y [T*topk, H] fp32, then the stages' scratch
   const size_t cap_min = moe_align_capacity(T, topk, shape->num_experts, block_m);
-  uint16_t* h = static_cast<uint16_t*>(workspace);
-  float* y = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + round_up(cap_min * shape->intermediate * 2));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+  const size_t h_bytes = round_up(cap_min * shape->intermediate * 2);
+  float* y = reinterpret_cast<float*>(ws + h_bytes);
+  const size_t y_bytes = round_up((size_t)T * topk * shape->hidden * 4);
+  void* scratch = ws + h_bytes + y_bytes;
+  const size_t scratch_bytes = workspace_bytes - h_bytes - y_bytes;
   // Rows past cap_min are never live: num_tokens_post_padded <= cap_min.
-  st = w4a16_moe_gate_up(shape, x, T, topk, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
-                         block_m, w13_packed, h, stream);
+  st = w4a16_moe_gate_up(shape, x, T, topk, topk_ids, sorted_token_ids, (int32_t)cap_min, expert_ids,
+                         num_tokens_post_padded, block_m, w13_packed, h, scratch, scratch_bytes, stream);
   if (st != W4A16_OK) return st;
   st = w4a16_moe_down(shape, T, topk, h, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
-                      block_m, w2_packed, y, stream);
+                      block_m, w2_packed, y, scratch, scratch_bytes, stream);
   if (st != W4A16_OK) return st;
   return w4a16_moe_combine(shape, T, topk, topk_ids, topk_weights, y, out, stream);
 }

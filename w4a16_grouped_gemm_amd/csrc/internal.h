@@ -29,16 +29,45 @@ namespace w4a16 {
 // Scales: one 64-entry unit of bf16 per (e, nb, g), same unit order; entry
 // 4 * (l & 15) + c is the scale of column 16c + (l & 15), so a lane reads its
 // four scales as one 8-byte load.
+//
+// Normalised scales (read by the fp16-operand tiled GEMM): the same units in
+// fp16, holding s * 2^-E_n, where E_n (int32 per expert and packed channel
+// 64 nb + 16 c + j, stored after them) is the unbiased exponent of the
+// channel's largest |s|. The normalised scales are exact copies of the bf16
+// ones down to 2^-17 of the channel's largest (smaller ones round to the fp16
+// subnormal grid).
+//
+// A projection's packed buffer is four 256-byte aligned regions: nibbles,
+// bf16 scales, fp16 scales, channel exponents (see packed_regions).
 // ---------------------------------------------------------------------------
 constexpr int kGroup = 32;
 constexpr int kNBlock = 64;
 constexpr int kNibUnitBytes = 1024;
 constexpr int kScaleUnitElems = 64;
 
+struct PackedRegions {
+  size_t nib, s_bf16, s_f16, cexp, total;  // byte offsets of the regions, total size
+};
+inline size_t round_up256(size_t v) { return (v + 255) / 256 * 256; }
+inline PackedRegions packed_regions(size_t E, size_t N, size_t K) {
+  PackedRegions r;
+  r.nib = 0;
+  r.s_bf16 = round_up256(E * N * K / 2);
+  r.s_f16 = r.s_bf16 + round_up256(E * N * (K / kGroup) * 2);
+  r.cexp = r.s_f16 + round_up256(E * N * (K / kGroup) * 2);
+  r.total = r.cexp + round_up256(E * N * 4);
+  return r;
+}
+
 struct GemmParams {
   const uint16_t* a;       // gate_up: x [T, H]; down: h [capacity, I]
   const uint8_t* wq;       // packed nibbles of this projection, all experts
-  const uint16_t* ws;      // packed scales of this projection, all experts
+  const uint16_t* ws;      // packed bf16 scales of this projection, all experts
+  const uint16_t* ws16;    // packed normalised fp16 scales (tiled path)
+  const int32_t* col_exp;  // channel exponents E_n [E, N] (tiled path)
+  const int32_t* row_exp;  // A row exponents (tiled path, set by its launcher)
+  const uint16_t* a16;     // fp16 copy of the A rows (tiled path, set by its launcher)
+  const int32_t* topk_ids; // [T, topk] (gate_up on the tiled path)
   const int32_t* sorted;   // sorted_token_ids [capacity]
   const int32_t* expert_ids;
   const int32_t* ntpp;     // num_tokens_post_padded (device)
@@ -60,15 +89,20 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t block_
                         void* workspace, hipStream_t stream);
 size_t align_workspace_bytes(int64_t n, int32_t E);
 
+// Writes all four regions of one projection's packed buffer.
 hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t N, int32_t K,
-                         int32_t interleave_I, uint8_t* out_q, uint16_t* out_s, hipStream_t stream);
+                         int32_t interleave_I, uint8_t* packed, hipStream_t stream);
 
-hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream);
+// `scratch` (device, >= gemm_scratch_bytes) is used by the tiled path only.
+hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, void* scratch, hipStream_t stream);
 
-// Tiled (LDS-staged, 128 x 256 tile) variant for block_m == 128; used by
-// launch_moe_gemm when the shape fits it.
+// Tiled (LDS-staged, 128 x 256 tile, fp16 operands) variant for block_m == 128;
+// used by launch_moe_gemm when the shape fits it. It first converts the A rows
+// it reads to fp16 (with a power-of-two factor per row) into `scratch`, which
+// must hold tiled_scratch_bytes(rows, K): rows = T for gate_up, capacity for down.
 bool tiled_gemm_supported(int32_t block_m, const GemmParams& p);
-hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, hipStream_t stream);
+size_t tiled_scratch_bytes(int64_t rows, int32_t K);
+hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, void* scratch, hipStream_t stream);
 
 // Weight-streaming variant for block_m 16..64 with LDS rings for A and scales;
 // used when N is a multiple of 256 and K / 32 a multiple of 4.

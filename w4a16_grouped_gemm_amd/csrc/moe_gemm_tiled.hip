@@ -6,27 +6,45 @@
 // K2.x용 더 빠른 INT4 MoE 커널 출시: Chord", section "핵심 기여"; and the
 // small- vs large-batch pipelines of the Humming announcement, "Humming:
 // vLLM과 Ant Group, 양자화 추론을 위한 범용 커널 라이브러리 오픈소스 공개",
-// section "워크로드별 튜닝 및 JIT 컴파일"). The arithmetic is the same as the
-// streaming kernel's: exact integer operands (q + 136) on
-// v_mfma_f32_16x16x32_bf16 with a -136 * sum(x) correction in the C input,
-// then one fp32 FMA per output per 32-wide group for the BF16 group scale.
+// section "워크로드별 튜닝 및 JIT 컴파일").
 //
-// Tile: a 512-thread workgroup (8 waves, 2 x 4) computes 128 rows x 256
-// channels (four 64-channel n-blocks) over the whole reduction; each wave owns
-// 64 rows x one n-block. The K loop moves in stages of two groups (64 k):
-//   A  128 rows x 64 k of bf16 (16 KiB), gathered through sorted_token_ids,
-//   B  4 n-blocks x 2 groups of packed nibbles (8 KiB) and their scales (1 KiB),
-// all copied global -> LDS by global_load_lds_dwordx4 / _dword (no VGPRs in
-// flight), into a ring of kStages stages. LDS A is laid out fragment-major
-// (row block, group, lane, 16 bytes), so every MFMA operand is one
-// conflict-free ds_read_b128 per lane. The hardware's in-order vmcnt tracks
-// the copies: a wave waits until its copies of the stage it is about to use
-// have landed, then a workgroup barrier makes all waves' copies visible; the
-// same barrier proves that the slot refilled next has been consumed.
+// Arithmetic: fp16 operands on v_mfma_f32_16x16x32_f16, fp32 accumulation.
+// Both operands are exact images of the bf16/int4 inputs:
+//   * weights: q * s' where s' = s * 2^-E_n is the group scale normalised by a
+//     power of two per output channel (E_n from the channel's largest scale).
+//     q has at most 4 significant bits and s' at most 8, so q * s' is an exact
+//     fp16 value; it is formed with two exact packed-fp16 operations from the
+//     code (q + 8) OR-ed into the mantissa of fp16 1024.0.
+//   * activations: rows converted by rows_to_f16 with a power-of-two row factor
+//     (largest element mapped into [2^14, 2^15)).
+// Every product is exact, the sum is fp32 (as the scalar definition), and the
+// epilogue restores 2^(row exponent + E_n) with one ldexp per output. No
+// per-group rescale is needed: the group scale lives in the B operand.
+// The one approximation is fp16's subnormal floor: an activation more than 2^38
+// below its row's largest, or a scale more than 2^17 below its channel's
+// largest, is rounded to the fp16 subnormal grid (absolute error at most 2^-39
+// of the row's largest element, resp. 2^-25 of the channel's largest scale),
+// far below the rounding of the fp32 sum itself. SiLU's exponential tail puts
+// such tiny elements in h routinely; they cannot move a result that the fp32
+// sum resolves.
+//
+// Tile: a 512-thread workgroup (8 waves) computes 128 rows x 256 channels (four
+// 64-channel n-blocks) over the whole reduction. Wave w owns all 128 rows and
+// two 16-channel column blocks of n-block w / 2: blocks (w & 1) and (w & 1) + 2,
+// i.e. matching gate and up channels for the gate_up projection. Each weight is
+// dequantised by exactly one wave. The K loop moves in stages of two groups:
+//   A  128 rows x 64 k of fp16 (16 KiB), gathered through sorted_token_ids,
+//   B  4 n-blocks x 2 groups of packed nibbles (8 KiB) and fp16 scales (1 KiB),
+// copied global -> LDS by global_load_lds_dwordx4 / _dword (no VGPRs in flight)
+// into a ring of kStages stages. LDS A is fragment-major (row block, group,
+// lane, 16 bytes): every MFMA operand is one conflict-free ds_read_b128. The
+// in-order vmcnt tracks the copies: a wave waits for its own copies of the
+// stage it is about to use, then a workgroup barrier makes every wave's copies
+// visible; the same barrier proves the slot refilled next has been consumed.
 //
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8, and the tiles an
-// XCD runs are the n-tiles of the row blocks mb = xcd (mod 8), so the row
-// block's A tile (gathered activations) is shared through that XCD's L2.
+// XCD runs are the n-tiles of the row blocks mb = xcd (mod 8), so a row block's
+// A tile is shared through that XCD's L2.
 #include "internal.h"
 
 #include <algorithm>
@@ -34,16 +52,17 @@
 namespace w4a16 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kThreads = 512;
-constexpr int kWaves = 8;
 constexpr int kStages = 3;           // LDS ring depth
 constexpr int kTileM = 128;
+constexpr int kRowBlocks = kTileM / 16;
 constexpr int kTileNBlocks = 4;      // 4 x 64 = 256 channels
 constexpr int kStageGroups = 2;      // 64 k per stage
 constexpr int kABytes = kTileM * kStageGroups * kGroup * 2;                  // 16 KiB
@@ -56,10 +75,7 @@ constexpr int kCopiesPerWaveStage = 4;  // 2 A blocks + 1 nibble unit + 1 scale 
 constexpr int kNonTemporal = 2;
 
 constexpr uint32_t kCodeMask = 0x000F000Fu;
-constexpr uint32_t kBf16_128 = 0x43004300u;
-constexpr uint32_t kBf16_Minus136 = 0xC308C308u;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+constexpr uint32_t kF16_1024 = 0x64006400u;  // fp16 1024.0 in both halves
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
   uint32_t r;
@@ -67,21 +83,32 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
   return r;
 }
 
-__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w, uint32_t magic) {
+// Eight codes of one column block -> fp16 (code - 8) * s, exactly: OR-ing the
+// code into fp16 1024.0 gives 1024 + code, the subtraction of 1032 is exact
+// (small integers), and so is the product with s (4 x 8 significant bits).
+__device__ __forceinline__ f16x8 dequant(uint32_t w, f16x2 s2, uint32_t magic) {
+  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   u32x4 r;
-  r.x = and_or(w, kCodeMask, magic);
-  r.y = and_or(w >> 4, kCodeMask, magic);
-  r.z = and_or(w >> 8, kCodeMask, magic);
-  r.w = and_or(w >> 12, kCodeMask, magic);
-  return as_bf16x8(r);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f16x2 t = __builtin_bit_cast(f16x2, and_or(w >> (4 * d), kCodeMask, magic));
+    r[d] = __builtin_bit_cast(uint32_t, (t + bias) * s2);
+  }
+  return __builtin_bit_cast(f16x8, r);
 }
 
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx4 mfma16(f16x8 a, f16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ f16x2 splat(uint32_t bits16) {
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return f16x2{h, h};
 }
 
 // Wait until at most N of this wave's vector-memory operations are pending.
@@ -104,19 +131,18 @@ __device__ __forceinline__ void ring_barrier() {
 struct TileCtx {
   const uint8_t* a_src;  // this lane's A copy source (row start + 16-byte k offset)
   const uint8_t* wq;     // nibble units of this wave's copy n-block, group 0
-  const uint8_t* ws;     // scale units of this wave's copy n-block, group 0
-  int copy_rb;           // row block this wave copies
+  const uint8_t* ws;     // fp16 scale units of this wave's copy n-block, group 0
   int copy_nb, copy_j;   // nibble / scale unit this wave copies: n-block, group in stage
 };
 
 // Issue this wave's copies of stage `s` (groups 2s, 2s+1) into ring slot `slot`.
-__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int slot, int s, int lane) {
+__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int slot, int s, int wave, int lane) {
   uint8_t* base = ring + slot * kStageBytes;
   const int g0 = s * kStageGroups;
 #pragma unroll
   for (int j = 0; j < kStageGroups; ++j) {
     const uint8_t* src = c.a_src + (int64_t)(g0 + j) * (kGroup * 2);
-    __builtin_amdgcn_global_load_lds(src, LDS_PTR(base + (c.copy_rb * kStageGroups + j) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, LDS_PTR(base + (wave * kStageGroups + j) * 1024), 16, 0, 0);
   }
   {
     const uint8_t* src = c.wq + (int64_t)(g0 + c.copy_j) * kNibUnitBytes + 16 * lane;
@@ -133,23 +159,92 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int
   }
 }
 
+// The K loop and epilogue of one tile for a wave owning column blocks HALF and
+// HALF + 2 of n-block wn (HALF is wave-uniform, so it is a template argument:
+// no per-group selects).
+template <int MODE, int HALF>
+__device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c, uint8_t* ring, int nstages, int mb,
+                                          int nt, int e, int wave, int lane) {
+  const int wn = wave >> 1;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  uint32_t magic = kF16_1024;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
+  floatx4 acc[kRowBlocks][2];
+#pragma unroll
+  for (int rb = 0; rb < kRowBlocks; ++rb) acc[rb][0] = acc[rb][1] = zero4;
+
+  // the previous tile's reads of every slot are done before it is refilled
+  ring_barrier();
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nstages) issue_stage(c, ring, s, s, wave, lane);
+
+  for (int s = 0; s < nstages; ++s) {
+    // own copies of stage s landed (later stages may still be in flight) ...
+    if (s + kStages - 2 < nstages) wait_vmcnt<(kStages - 2) * kCopiesPerWaveStage>();
+    else wait_vmcnt<0>();
+    // ... and everyone's; everyone also finished reading stage s - 1
+    ring_barrier();
+    if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave, lane);
+
+    const uint8_t* base = ring + (s % kStages) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+      const u32x4 nib = *reinterpret_cast<const u32x4*>(base + kABytes + (wn * kStageGroups + j) * 1024 + 16 * lane);
+      const u32x2 sc = *reinterpret_cast<const u32x2*>(base + kABytes + kBBytes + (wn * kStageGroups + j) * 128 +
+                                                       8 * (lane & 15));
+      // entry 4 * (lane & 15) + c of the unit is column block c's scale
+      const f16x8 w0 = dequant(HALF ? nib.y : nib.x, splat(HALF ? sc.x >> 16 : sc.x & 0xFFFFu), magic);
+      const f16x8 w1 = dequant(HALF ? nib.w : nib.z, splat(HALF ? sc.y >> 16 : sc.y & 0xFFFFu), magic);
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const f16x8 a =
+            __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(base + (rb * kStageGroups + j) * 1024 + 16 * lane));
+        acc[rb][0] = mfma16(a, w0, acc[rb][0]);
+        acc[rb][1] = mfma16(a, w1, acc[rb][1]);
+      }
+    }
+  }
+
+  // Epilogue: rows 16 rb + 4 (lane >> 4) + i of the tile; packed channels
+  // 64 nb + 16 c + (lane & 15) for c = HALF, HALF + 2.
+  const int nb = nt * kTileNBlocks + wn;
+  const int pc0 = nb * kNBlock + 16 * HALF + (lane & 15);
+  const int32_t* cexp = p.col_exp + (int64_t)e * p.N;
+  const int ce0 = cexp[pc0], ce1 = cexp[pc0 + 32];
+#pragma unroll
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + i;
+      const int id = p.sorted[prow];
+      if ((unsigned)id >= (unsigned)p.n_slots) continue;
+      const int re = p.row_exp[MODE == kGateUp ? id / p.topk : prow];
+      const float v0 = __builtin_amdgcn_ldexpf(acc[rb][0][i], re + ce0);
+      const float v1 = __builtin_amdgcn_ldexpf(acc[rb][1][i], re + ce1);
+      if (MODE == kGateUp) {
+        __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + 16 * HALF + (lane & 15);
+        h[0] = (__bf16)silu_mul(v0, v1);
+      } else {
+        float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + pc0;
+        y[0] = v0;
+        y[32] = v1;
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   const int lane = (int)threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int wm = wave >> 2;  // 64-row half of the tile
-  const int wn = wave & 3;   // n-block of the tile
   const int ntpp = min(*p.ntpp, p.capacity);
   const int n_mblocks = ntpp / kTileM;
   const int NB = p.N / kNBlock;
   const int NT = NB / kTileNBlocks;  // n-tiles per row block
   const int G = p.K / kGroup;
   const int nstages = G / kStageGroups;
-  uint32_t magic = kBf16_128;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
-  const bf16x8 minus136 = as_bf16x8(u32x4{kBf16_Minus136, kBf16_Minus136, kBf16_Minus136, kBf16_Minus136});
-  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // XCD-aware order: local tile index q of XCD x covers row block x + 8 (q / NT).
   const int xcd = (int)blockIdx.x & 7;
@@ -161,9 +256,9 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
     const int e = p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
 
-    // this wave copies A row block `wave` (rows 16 wave .. 16 wave + 15)
+    // this wave copies A row block `wave` (rows 16 wave .. 16 wave + 15);
+    // padding rows read the block's first row (their results are discarded)
     TileCtx c;
-    c.copy_rb = wave;
     c.copy_nb = wave >> 1;
     c.copy_j = wave & 1;
     {
@@ -177,73 +272,72 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
       } else {
         src = real ? prow : mb * kTileM;
       }
-      c.a_src = reinterpret_cast<const uint8_t*>(p.a + src * p.K) + 16 * (lane >> 4);
+      c.a_src = reinterpret_cast<const uint8_t*>(p.a16 + src * p.K) + 16 * (lane >> 4);
     }
     const int64_t unit_copy = ((int64_t)e * NB + nt * kTileNBlocks + c.copy_nb) * G;
     c.wq = p.wq + unit_copy * kNibUnitBytes;
-    c.ws = reinterpret_cast<const uint8_t*>(p.ws + unit_copy * kScaleUnitElems);
+    c.ws = reinterpret_cast<const uint8_t*>(p.ws16 + unit_copy * kScaleUnitElems);
 
-    floatx4 acc[4][4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = zero4;
+    if (wave & 1) tile_body<MODE, 1>(p, c, ring, nstages, mb, nt, e, wave, lane);
+    else tile_body<MODE, 0>(p, c, ring, nstages, mb, nt, e, wave, lane);
+  }
+}
 
-    // the previous tile's reads of every slot are done before it is refilled
-    ring_barrier();
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      if (s < nstages) issue_stage(c, ring, s, s, lane);
-
-    for (int s = 0; s < nstages; ++s) {
-      // own copies of stage s landed (later stages may still be in flight) ...
-      if (s + kStages - 2 < nstages) wait_vmcnt<(kStages - 2) * kCopiesPerWaveStage>();
-      else wait_vmcnt<0>();
-      // ... and everyone's; everyone also finished reading stage s - 1
-      ring_barrier();
-      if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, lane);
-
-      const uint8_t* base = ring + (s % kStages) * kStageBytes;
-#pragma unroll
-      for (int j = 0; j < kStageGroups; ++j) {
-        const u32x4 nib = *reinterpret_cast<const u32x4*>(base + kABytes + (wn * kStageGroups + j) * 1024 + 16 * lane);
-        const u32x2 sc = *reinterpret_cast<const u32x2*>(base + kABytes + kBBytes + (wn * kStageGroups + j) * 128 +
-                                                         8 * (lane & 15));
-        const float scale[4] = {__uint_as_float(sc.x << 16), __uint_as_float(sc.x & 0xFFFF0000u),
-                                __uint_as_float(sc.y << 16), __uint_as_float(sc.y & 0xFFFF0000u)};
-        bf16x8 w[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) w[cb] = codes_to_bf16(nib[cb], magic);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const bf16x8 a = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(base + ((4 * wm + rb) * kStageGroups + j) * 1024 + 16 * lane));
-          const floatx4 corr = mfma16(a, minus136, zero4);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] += scale[cb] * mfma16(a, w[cb], corr);
-        }
-      }
+// Rows of a bf16 matrix -> fp16 with a power-of-two factor per row: the row's
+// largest magnitude is mapped into [2^14, 2^15), which keeps every element
+// exact unless it is more than 2^38 below that largest one (then it rounds on
+// the fp16 subnormal grid, an error below 2^-39 of the row's largest element).
+// dst[r] = src[r] * 2^-row_exp[r]. One workgroup per row; rows that no GEMM
+// reads are skipped: by token (a resident topk id) or by aligned row (real slot).
+template <bool BY_TOKEN>
+__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ src, int32_t K, int32_t nrows,
+                                                          const int32_t* __restrict__ topk_ids, int32_t topk,
+                                                          int32_t E, const int32_t* __restrict__ sorted,
+                                                          const int32_t* __restrict__ ntpp, int32_t n_slots,
+                                                          uint16_t* __restrict__ dst, int32_t* __restrict__ row_exp) {
+  __shared__ uint32_t red[4];
+  const int tid = (int)threadIdx.x;
+  const int chunks = K / 8;
+  const int live = BY_TOKEN ? nrows : min(*ntpp, nrows);
+  for (int r = (int)blockIdx.x; r < live; r += (int)gridDim.x) {
+    bool need = false;
+    if (BY_TOKEN) {
+      for (int j = 0; j < topk; ++j) need |= (unsigned)topk_ids[(int64_t)r * topk + j] < (unsigned)E;
+    } else {
+      need = (unsigned)sorted[r] < (unsigned)n_slots;
     }
-
-    // Epilogue: wave rows 64 wm + 16 rb + 4 (lane >> 4) + i, n-block nt * 4 + wn.
-    const int nb = nt * kTileNBlocks + wn;
+    if (!need) continue;  // uniform: every thread read the same values
+    const u32x4* row = reinterpret_cast<const u32x4*>(src + (int64_t)r * K);
+    // largest |x| as a bf16 bit pattern (sign cleared: integer order = magnitude order)
+    uint32_t mx = 0;
+    for (int ch = tid; ch < chunks; ch += 256) {
+      const u32x4 v = row[ch];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+      for (int d = 0; d < 4; ++d) mx = max(mx, max(v[d] & 0x7FFFu, (v[d] >> 16) & 0x7FFFu));
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int prow = mb * kTileM + 64 * wm + 16 * rb + 4 * (lane >> 4) + i;
-        const int id = p.sorted[prow];
-        if ((unsigned)id >= (unsigned)p.n_slots) continue;
-        if (MODE == kGateUp) {
-          __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + (lane & 15);
-          h[0] = (__bf16)silu_mul(acc[rb][0][i], acc[rb][2][i]);
-          h[16] = (__bf16)silu_mul(acc[rb][1][i], acc[rb][3][i]);
-        } else {
-          float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + nb * kNBlock + (lane & 15);
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    __syncthreads();  // red is reused by the next row
+    // unbiased exponent of the largest element (subnormals count as -126)
+    const int ef = (int)(mx >> 7);
+    const int ex = mx == 0 ? 14 : (ef == 0 ? -126 : ef - 127);
+    const int e = ex - 14;
+    if (tid == 0) row_exp[r] = e;
+    u32x4* out = reinterpret_cast<u32x4*>(dst + (int64_t)r * K);
+    for (int ch = tid; ch < chunks; ch += 256) {
+      const u32x4 v = row[ch];
+      u32x4 o;
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) y[16 * cb] = acc[rb][cb][i];
-        }
+      for (int d = 0; d < 4; ++d) {
+        const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(v[d] << 16), -e);
+        const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(v[d] & 0xFFFF0000u), -e);
+        const f16x2 h = {(_Float16)lo, (_Float16)hi};
+        o[d] = __builtin_bit_cast(uint32_t, h);
       }
+      out[ch] = o;
     }
   }
 }
@@ -279,8 +373,31 @@ bool tiled_gemm_supported(int32_t block_m, const GemmParams& p) {
   return block_m == kTileM && (p.K / kGroup) % kStageGroups == 0 && p.N % (kNBlock * kTileNBlocks) == 0;
 }
 
-hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, hipStream_t stream) {
-  return mode == kGateUp ? launch_tiled_mode<kGateUp>(p, stream) : launch_tiled_mode<kDown>(p, stream);
+size_t tiled_scratch_bytes(int64_t rows, int32_t K) {
+  const size_t a = (size_t)rows * K * 2;
+  return (a + 255) / 256 * 256 + (size_t)rows * 4;
+}
+
+hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, void* scratch, hipStream_t stream) {
+  // scratch: fp16 A rows [rows, K] (256-byte aligned), then int32 row exponents [rows]
+  const int64_t rows = mode == kGateUp ? (int64_t)p.n_slots / p.topk : p.capacity;
+  uint16_t* a16 = static_cast<uint16_t*>(scratch);
+  int32_t* rexp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(scratch) + ((size_t)rows * p.K * 2 + 255) / 256 * 256);
+  if (rows > 0) {
+    const int grid = (int)std::min<int64_t>(rows, (int64_t)device_cu_count() * 16);
+    if (mode == kGateUp)
+      hipLaunchKernelGGL(rows_to_f16_kernel<true>, dim3(grid), dim3(256), 0, stream, p.a, p.K, (int32_t)rows,
+                         p.topk_ids, p.topk, p.E, p.sorted, p.ntpp, p.n_slots, a16, rexp);
+    else
+      hipLaunchKernelGGL(rows_to_f16_kernel<false>, dim3(grid), dim3(256), 0, stream, p.a, p.K, (int32_t)rows,
+                         p.topk_ids, p.topk, p.E, p.sorted, p.ntpp, p.n_slots, a16, rexp);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  GemmParams q = p;
+  q.a16 = a16;
+  q.row_exp = rexp;
+  return mode == kGateUp ? launch_tiled_mode<kGateUp>(q, stream) : launch_tiled_mode<kDown>(q, stream);
 }
 
 }  // namespace w4a16

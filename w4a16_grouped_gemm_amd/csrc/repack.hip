@@ -69,10 +69,39 @@ __global__ void repack_scales_kernel(const uint16_t* __restrict__ s, uint16_t* _
   }
 }
 
+// Normalised fp16 scales and channel exponents: one thread per (expert, packed
+// channel). E_n is the unbiased exponent of the channel's largest |s| (a zero
+// channel gets 0, bf16 subnormals count as 2^-126), and every group scale is
+// stored as fp16(s * 2^-E_n), a value in (-2, 2).
+__global__ void repack_f16_scales_kernel(const uint16_t* __restrict__ s, uint16_t* __restrict__ out,
+                                         int32_t* __restrict__ col_exp, int N, int K, int interleave_I,
+                                         int64_t total) {
+  const int G = K / kGroup;
+  const int NB = N / kNBlock;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total; d += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = d / N;
+    const int pc = (int)(d % N);
+    const int nb = pc / kNBlock, c = (pc % kNBlock) / 16, j = pc % 16;
+    const uint16_t* src = s + (e * N + source_row(nb, c, j, interleave_I)) * (int64_t)G;
+    uint32_t mx = 0;
+    for (int g = 0; g < G; ++g) mx = max(mx, (uint32_t)(src[g] & 0x7FFFu));
+    const int ef = (int)(mx >> 7);
+    const int ex = mx == 0 ? 0 : (ef == 0 ? -126 : ef - 127);
+    col_exp[d] = ex;
+    for (int g = 0; g < G; ++g) {
+      const float v = __builtin_amdgcn_ldexpf(__uint_as_float((uint32_t)src[g] << 16), -ex);
+      out[((e * NB + nb) * G + g) * kScaleUnitElems + 4 * j + c] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t N, int32_t K, int32_t interleave_I,
-                         uint8_t* out_q, uint16_t* out_s, hipStream_t stream) {
+                         uint8_t* packed, hipStream_t stream) {
+  const PackedRegions r = packed_regions(E, N, K);
+  uint8_t* out_q = packed + r.nib;
+  uint16_t* out_s = reinterpret_cast<uint16_t*>(packed + r.s_bf16);
   const int64_t dwords = (int64_t)E * N * K / 8;
   const int64_t scales = (int64_t)E * N * (K / kGroup);
   const int grid_q = (int)std::min<int64_t>(65536, (dwords + 255) / 256);
@@ -82,6 +111,13 @@ hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(repack_scales_kernel, dim3(grid_s), dim3(256), 0, stream, s, out_s, N, K, interleave_I, scales);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t cols = (int64_t)E * N;
+  const int grid_c = (int)std::min<int64_t>(65536, (cols + 255) / 256);
+  hipLaunchKernelGGL(repack_f16_scales_kernel, dim3(grid_c), dim3(256), 0, stream, s,
+                     reinterpret_cast<uint16_t*>(packed + r.s_f16), reinterpret_cast<int32_t*>(packed + r.cexp), N, K,
+                     interleave_I, cols);
   return hipGetLastError();
 }
 
