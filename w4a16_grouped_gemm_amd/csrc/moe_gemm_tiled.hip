@@ -70,6 +70,8 @@ constexpr int kBBytes = kTileNBlocks * kStageGroups * kNibUnitBytes;         // 
 constexpr int kSBytes = kTileNBlocks * kStageGroups * kScaleUnitElems * 2;   // 1 KiB
 constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
 constexpr int kCopiesPerWaveStage = 4;  // 2 A blocks + 1 nibble unit + 1 scale unit
+// A fragments read ahead of the MFMAs that use them
+constexpr int kAhead = 4;
 // Weights and scales are read once per tile: copied with the non-temporal
 // policy (operand 2 = nt) so they do not evict the A tile shared through L2.
 constexpr int kNonTemporal = 2;
@@ -187,23 +189,51 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     ring_barrier();
     if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave, lane);
 
+    // Software pipeline inside the stage: while a group's MFMAs run, the wave
+    // reads the A fragments kAhead row blocks ahead (wrapping into the next
+    // group) and dequantises the next group's weights; each MFMA pair sits in
+    // its own scheduling region so the compiler keeps that interleave.
     const uint8_t* base = ring + (s % kStages) * kStageBytes;
+    const auto lds_a = [&](int rb, int j) {
+      return __builtin_bit_cast(f16x8,
+                                *reinterpret_cast<const u32x4*>(base + (rb * kStageGroups + j) * 1024 + 16 * lane));
+    };
+    u32x4 nib[kStageGroups];
+    u32x2 sc[kStageGroups];
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) {
-      const u32x4 nib = *reinterpret_cast<const u32x4*>(base + kABytes + (wn * kStageGroups + j) * 1024 + 16 * lane);
-      const u32x2 sc = *reinterpret_cast<const u32x2*>(base + kABytes + kBBytes + (wn * kStageGroups + j) * 128 +
-                                                       8 * (lane & 15));
+      nib[j] = *reinterpret_cast<const u32x4*>(base + kABytes + (wn * kStageGroups + j) * 1024 + 16 * lane);
       // entry 4 * (lane & 15) + c of the unit is column block c's scale
-      const f16x8 w0 = dequant(HALF ? nib.y : nib.x, splat(HALF ? sc.x >> 16 : sc.x & 0xFFFFu), magic);
-      const f16x8 w1 = dequant(HALF ? nib.w : nib.z, splat(HALF ? sc.y >> 16 : sc.y & 0xFFFFu), magic);
+      sc[j] = *reinterpret_cast<const u32x2*>(base + kABytes + kBBytes + (wn * kStageGroups + j) * 128 +
+                                             8 * (lane & 15));
+    }
+    const auto deq0 = [&](int j) {
+      return dequant(HALF ? nib[j].y : nib[j].x, splat(HALF ? sc[j].x >> 16 : sc[j].x & 0xFFFFu), magic);
+    };
+    const auto deq1 = [&](int j) {
+      return dequant(HALF ? nib[j].w : nib[j].z, splat(HALF ? sc[j].y >> 16 : sc[j].y & 0xFFFFu), magic);
+    };
+    f16x8 a[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kAhead; ++rb) a[rb] = lds_a(rb, 0);
+    f16x8 w0 = deq0(0), w1 = deq1(0);
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+      f16x8 v0 = w0, v1 = w1;
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const f16x8 a =
-            __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(base + (rb * kStageGroups + j) * 1024 + 16 * lane));
-        acc[rb][0] = mfma16(a, w0, acc[rb][0]);
-        acc[rb][1] = mfma16(a, w1, acc[rb][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[rb][0] = mfma16(a[rb], w0, acc[rb][0]);
+        acc[rb][1] = mfma16(a[rb], w1, acc[rb][1]);
+        if (rb + kAhead < kRowBlocks) a[rb + kAhead] = lds_a(rb + kAhead, j);
+        else if (j + 1 < kStageGroups) a[rb + kAhead - kRowBlocks] = lds_a(rb + kAhead - kRowBlocks, j + 1);
+        if (j + 1 < kStageGroups && rb == 1) v0 = deq0(j + 1);
+        if (j + 1 < kStageGroups && rb == 3) v1 = deq1(j + 1);
       }
+      w0 = v0;
+      w1 = v1;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue: rows 16 rb + 4 (lane >> 4) + i of the tile; packed channels
