@@ -90,6 +90,15 @@ def cpu_baseline(c, target_slots: int):
                       f"{dt:.2f} s wall, scaled by slots to the whole layer"}
 
 
+def gemm_kernel_name(block_m: int, N: int, K: int) -> str:
+    """The GEMM kernel the library dispatches to for this block_m and shape."""
+    if block_m == 128 and N % 256 == 0 and (K // 32) % 2 == 0:
+        return "moe_gemm_tiled_kernel"
+    if block_m in (16, 32, 64) and N % 256 == 0 and (K // 32) % 4 == 0:
+        return "moe_gemm_stream_lds_kernel"
+    return "moe_gemm_stream_kernel"
+
+
 def stored_traffic(workload: str, kernel: str, launches_per_step: int = 1):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the current kernel sources (else None)."""
@@ -167,18 +176,23 @@ def main():
         w.moe_align(ids, E, bm, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"], None,
                     buf["workspace"])
 
+    srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+
     def stages(ev):
+        # one event between consecutive stages: align, prepare_x, gate_up, prepare_h, down, combine
         ev[0].record()
         align()
         ev[1].record()
-        w.w4a16_moe_gate_up(shape, x, ids, buf["sorted_token_ids"], buf["expert_ids"],
-                            buf["num_tokens_post_padded"], bm, w13p, h, scratch)
+        w.w4a16_moe_prepare_x(shape, x, ids, bm, scratch)
         ev[2].record()
-        w.w4a16_moe_down(shape, T, topk, h, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"],
-                         bm, w2p, y, scratch)
+        w.w4a16_moe_gate_up(shape, x, T, topk, srt, eid, ntpp, bm, w13p, h, scratch)
         ev[3].record()
-        w.w4a16_moe_combine(shape, ids, wts, y, out)
+        w.w4a16_moe_prepare_h(shape, T, topk, h, srt, ntpp, bm, scratch)
         ev[4].record()
+        w.w4a16_moe_down(shape, T, topk, h, srt, eid, ntpp, bm, w2p, y, scratch)
+        ev[5].record()
+        w.w4a16_moe_combine(shape, ids, wts, y, out)
+        ev[6].record()
 
     def forward_step(ev):
         ev[0].record()
@@ -192,7 +206,7 @@ def main():
     forward_step(mk(2))
     torch.cuda.synchronize()
     ref = out.clone()
-    stages(mk(5))
+    stages(mk(7))
     torch.cuda.synchronize()
     assert torch.equal(ref, out), "staged sequence differs from w4a16_moe_forward"
 
@@ -200,7 +214,7 @@ def main():
         if not args.warm:
             flush()
         forward_step(mk(2))
-        stages(mk(5))
+        stages(mk(7))
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -218,20 +232,20 @@ def main():
     for i in range(args.steps):
         if not args.warm:
             flush()
-        ev = mk(5)
+        ev = mk(7)
         stages(ev)
         stage_ev.append(ev)
     torch.cuda.synchronize()
 
     layer_us = np.array([a.elapsed_time(b) * 1e3 for a, b in layer_ev])
-    st = np.array([[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(4)] for ev in stage_ev])
+    st = np.array([[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(6)] for ev in stage_ev])
     med = float(np.median(layer_us))
     kmed = np.median(st, axis=0)
     work = algorithmic_work(c)
     decode = work["layer_flops"] / max(1, work["layer_bytes"]) < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     layer_gbps = work["layer_bytes"] / (med * 1e-6) / 1e9
     layer_tflops = work["layer_flops"] / (med * 1e-6) / 1e12
-    gate_us = float(kmed[1])
+    gate_us = float(kmed[2])
     if decode:
         achieved = work["gate_up_bytes"] / (gate_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -240,7 +254,7 @@ def main():
         achieved = work["gate_up_flops"] / (gate_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    roof["kernel"] = "moe_gemm_stream_kernel<gate_up>"
+    roof["kernel"] = gemm_kernel_name(bm, 2 * I, H) + " (gate_up)"
     roof["traffic"] = stored_traffic(args.workload, "gate_up")
 
     result = {
@@ -263,8 +277,9 @@ def main():
         "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
         "layer_TFLOPs": round(layer_tflops, 2),
         "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
-        "kernels_us": {"align": round(float(kmed[0]), 2), "gate_up": round(gate_us, 2),
-                       "down": round(float(kmed[2]), 2), "combine": round(float(kmed[3]), 2)},
+        "kernels_us": {"align": round(float(kmed[0]), 2), "prepare_x": round(float(kmed[1]), 2),
+                       "gate_up": round(gate_us, 2), "prepare_h": round(float(kmed[3]), 2),
+                       "down": round(float(kmed[4]), 2), "combine": round(float(kmed[5]), 2)},
         "layer_us_p10_p90": [round(float(np.percentile(layer_us, 10)), 2), round(float(np.percentile(layer_us, 90)), 2)],
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "alg_bytes": work["layer_bytes"],

@@ -146,11 +146,11 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
  * scratch of the two GEMM stages (w4a16_moe_stage_workspace_bytes). */
 size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m);
 
-/* Device scratch bytes of w4a16_moe_gate_up and w4a16_moe_down (one region,
- * usable by both since they run one after the other): with block_m = 128 the
- * GEMMs first convert the activation rows they read to fp16 with a
- * power-of-two factor per row (T rows of x, then moe_align_capacity rows of h);
- * 0 for the other block_m values. */
+/* Device scratch bytes of the GEMM stages (one region shared by all of them,
+ * since they run one after the other): with block_m = 128 the GEMMs read fp16
+ * copies of their activation rows with a power-of-two factor per row, written
+ * by w4a16_moe_prepare_x (T rows of x) and w4a16_moe_prepare_h
+ * (moe_align_capacity rows of h); 0 for the other block_m values. */
 size_t w4a16_moe_stage_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m);
 
 /* out[t, :] = bf16( sum_j [0 <= topk_ids[t,j] < E] * topk_weights[t,j] *
@@ -178,23 +178,41 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
                       const void* w2_packed, uint16_t* out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* The three stages of w4a16_moe_forward, callable one by one (same arguments
- * and conventions; forward == gate_up, then down, then combine). gate_up and
- * down take a scratch region of w4a16_moe_stage_workspace_bytes (may be NULL
- * when that is 0), rewritten by each call.
+/* The stages of w4a16_moe_forward, callable one by one with the same
+ * arguments and conventions; forward == prepare_x, gate_up, prepare_h, down,
+ * combine. prepare_x, gate_up, prepare_h and down share a scratch region of
+ * w4a16_moe_stage_workspace_bytes (may be NULL when that is 0); each call may
+ * overwrite it, and the GEMMs read what the preceding prepare call left there.
  *
+ * prepare_x / prepare_h: with block_m = 128 the GEMMs run on exact fp16
+ *   operands (the weight side is the normalised fp16 scales of the packed
+ *   buffer). These stages write the activation side: every x row of a token
+ *   with a resident slot (prepare_x) and every real row of h (prepare_h) as
+ *   fp16(row * 2^-e) with e chosen per row so that its largest magnitude lands
+ *   in [2^14, 2^15), plus e. Exact except for elements more than 2^38 below
+ *   their row's largest, which round to the fp16 subnormal grid. No-ops for
+ *   the other block_m values.
  * gate_up: h[p, c] = bf16(silu(g[p, c]) * g[p, I + c]) for every real row p of
  *   the aligned order (sorted_token_ids[p] < T*topk), g = x[sorted[p]/topk] . W13^T.
  *   h: device bf16 [capacity, I]; padding rows are left untouched.
  * down: y[sorted[p], n] = h[p, :] . W2[e, n, :] for every real row p, in fp32.
  *   y: device fp32 [T*topk, H]; rows of non-resident slots are left untouched.
  * combine: out[t, n] = bf16(sum_j resident(t, j) * topk_weights[t, j] * y[t*topk+j, n]),
- *   summed in fp32 in j order. */
+ *   summed in fp32 in j order.
+ * Stage boundaries follow the layer definition of w4a16_moe_forward (the
+ * gate_up GEMM with its fused SiLU-and-mul, the down GEMM, the weighted top-k
+ * sum); the prepare stages are this implementation's operand conversion for
+ * the many-tokens-per-expert GEMM. */
+int w4a16_moe_prepare_x(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                        const int32_t* topk_ids, int32_t block_m, void* workspace, size_t workspace_bytes,
+                        void* stream);
 int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
-                      const int32_t* topk_ids, const int32_t* sorted_token_ids, int32_t capacity,
-                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int32_t block_m,
-                      const void* w13_packed, uint16_t* h, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed,
+                      uint16_t* h, void* workspace, size_t workspace_bytes, void* stream);
+int w4a16_moe_prepare_h(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
+                        const int32_t* sorted_token_ids, int32_t capacity, const int32_t* num_tokens_post_padded,
+                        int32_t block_m, void* workspace, size_t workspace_bytes, void* stream);
 int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
                    const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
                    const int32_t* num_tokens_post_padded, int32_t block_m, const void* w2_packed,

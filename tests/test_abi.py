@@ -105,21 +105,30 @@ def test_validation_status_codes(lib):
     # repack and stages
     assert lib.w4a16_repack(ctypes.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
-    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, FAKE, 3, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, 3, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
                                  None) == 3
-    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, None, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), None, 4, 2, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
                                  None) == 1
     assert lib.w4a16_moe_down(ctypes.byref(good), 4, 2, None, FAKE, 1000, FAKE, FAKE, 16, FAKE, FAKE, None, 0,
                               None) == 1
-    # block_m 128 needs the stages' scratch
+    assert lib.w4a16_moe_prepare_x(ctypes.byref(good), FAKE, 4, 2, None, 16, None, 0, None) == 1
+    assert lib.w4a16_moe_prepare_h(ctypes.byref(good), 4, 2, FAKE, FAKE, 3, FAKE, 16, None, 0, None) == 3
+    # block_m 16 needs no stage scratch: the prepare stages are no-ops
     assert w.w4a16_moe_stage_workspace_bytes(good, 4, 2, 16) == 0
+    assert lib.w4a16_moe_prepare_x(ctypes.byref(good), FAKE, 4, 2, FAKE, 16, None, 0, None) == 0
+    # block_m 128 needs it
     need = w.w4a16_moe_stage_workspace_bytes(good, 4, 2, 128)
     assert need > 0
     cap = w.moe_align_capacity(4, 2, 8, 128)
-    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, FAKE, cap, FAKE, FAKE, 128, FAKE, FAKE, None,
-                                 0, None) == 4
+    assert lib.w4a16_moe_prepare_x(ctypes.byref(good), FAKE, 4, 2, FAKE, 128, None, 0, None) == 4
+    assert lib.w4a16_moe_prepare_h(ctypes.byref(good), 4, 2, FAKE, FAKE, cap, FAKE, 128, FAKE, need - 1, None) == 4
+    assert lib.w4a16_moe_gate_up(ctypes.byref(good), FAKE, 4, 2, FAKE, cap, FAKE, FAKE, 128, FAKE, FAKE, None, 0,
+                                 None) == 4
     assert lib.w4a16_moe_down(ctypes.byref(good), 4, 2, FAKE, FAKE, cap, FAKE, FAKE, 128, FAKE, FAKE, FAKE, need - 1,
                               None) == 4
+    # shapes the tiled GEMMs do not take need none either (H = 320: down N % 256 != 0 but gate_up is tiled)
+    odd = w.make_shape(8, 320, 96)
+    assert w.w4a16_moe_stage_workspace_bytes(odd, 4, 2, 128) == 0
 
 
 def test_binding_raises(lib):

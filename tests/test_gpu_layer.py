@@ -36,6 +36,8 @@ SMALL = [
     ("single token", 1, 256, 128, 8, 8, 8, 16),
     ("bm64 skew", 150, 512, 160, 6, 2, 6, 64),
     ("bm128", 300, 384, 128, 4, 2, 4, 128),
+    ("bm128 mixed paths", 200, 320, 128, 4, 2, 4, 128),   # gate_up tiled, down streamed (H % 256 != 0)
+    ("bm128 streamed", 200, 512, 96, 4, 2, 4, 128),       # neither GEMM fits the tiled kernel
     ("many experts", 96, 256, 64, 200, 8, 256, 16),
 ]
 
@@ -97,21 +99,26 @@ def test_tokens_without_resident_expert_are_zero():
     parity(out, oracle_rows(c, ids=ids), "holes")
 
 
-def test_stages_equal_forward_and_deterministic():
-    c = synthetic.random_case("stages", T=90, H=512, I=128, E=10, topk=4, block_m=32, seed=11, E_global=20)
+@pytest.mark.parametrize("bm", [32, 128])
+def test_stages_equal_forward_and_deterministic(bm):
+    c = synthetic.random_case("stages", T=90, H=512, I=128, E=10, topk=4, block_m=bm, seed=11, E_global=20)
     d = DeviceCase(c)
-    ref = d.forward(32)
-    again = d.forward(32)
+    ref = d.forward(bm)
+    again = d.forward(bm)
     assert np.array_equal(ref, again)
-    buf = d.align(32)
+    buf = d.align(bm)
     cap = buf["sorted_token_ids"].numel()
     h = torch.zeros((cap, c.I), dtype=torch.int16, device="cuda")
     y = torch.zeros((c.T * c.topk, c.H), dtype=torch.float32, device="cuda")
     out = torch.full((c.T, c.H), -1, dtype=torch.int16, device="cuda")
-    w.w4a16_moe_gate_up(d.shape, d.x, d.ids, buf["sorted_token_ids"], buf["expert_ids"],
-                        buf["num_tokens_post_padded"], 32, d.w13p, h)
-    w.w4a16_moe_down(d.shape, c.T, c.topk, h, buf["sorted_token_ids"], buf["expert_ids"],
-                     buf["num_tokens_post_padded"], 32, d.w2p, y)
+    nws = w.w4a16_moe_stage_workspace_bytes(d.shape, c.T, c.topk, bm)
+    assert (nws > 0) == (bm == 128)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
+    srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+    w.w4a16_moe_prepare_x(d.shape, d.x, d.ids, bm, ws)
+    w.w4a16_moe_gate_up(d.shape, d.x, c.T, c.topk, srt, eid, ntpp, bm, d.w13p, h, ws)
+    w.w4a16_moe_prepare_h(d.shape, c.T, c.topk, h, srt, ntpp, bm, ws)
+    w.w4a16_moe_down(d.shape, c.T, c.topk, h, srt, eid, ntpp, bm, d.w2p, y, ws)
     w.w4a16_moe_combine(d.shape, d.ids, d.wts, y, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), ref)

@@ -107,13 +107,25 @@ def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def w4a16_moe_gate_up(shape: Shape, x, topk_ids, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                      block_m: int, w13_packed, h, workspace=None, stream=None):
+def w4a16_moe_prepare_x(shape: Shape, x, topk_ids, block_m: int, workspace=None, stream=None):
     T, topk = topk_ids.shape
-    _check(load().w4a16_moe_gate_up(ctypes.byref(shape), _p(x), T, topk, _p(topk_ids), _p(sorted_token_ids),
+    _check(load().w4a16_moe_prepare_x(ctypes.byref(shape), _p(x), T, topk, _p(topk_ids), block_m, _p(workspace),
+                                      _nbytes(workspace), _stream(stream)), "w4a16_moe_prepare_x")
+
+
+def w4a16_moe_gate_up(shape: Shape, x, T: int, topk: int, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                      block_m: int, w13_packed, h, workspace=None, stream=None):
+    _check(load().w4a16_moe_gate_up(ctypes.byref(shape), _p(x), T, topk, _p(sorted_token_ids),
                                     sorted_token_ids.numel(), _p(expert_ids), _p(num_tokens_post_padded), block_m,
                                     _p(w13_packed), _p(h), _p(workspace), _nbytes(workspace), _stream(stream)),
            "w4a16_moe_gate_up")
+
+
+def w4a16_moe_prepare_h(shape: Shape, T: int, topk: int, h, sorted_token_ids, num_tokens_post_padded, block_m: int,
+                        workspace=None, stream=None):
+    _check(load().w4a16_moe_prepare_h(ctypes.byref(shape), T, topk, _p(h), _p(sorted_token_ids),
+                                      sorted_token_ids.numel(), _p(num_tokens_post_padded), block_m, _p(workspace),
+                                      _nbytes(workspace), _stream(stream)), "w4a16_moe_prepare_h")
 
 
 def w4a16_moe_down(shape: Shape, T: int, topk: int, h, sorted_token_ids, expert_ids, num_tokens_post_padded,

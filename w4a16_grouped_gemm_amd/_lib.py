@@ -29,7 +29,9 @@ SIGNATURES = {
     "w4a16_moe_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_stage_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_forward": (ctypes.c_int, [P, P, I32, I32, P, P, P, I32, P, P, I32, P, P, P, P, SZ, P]),
-    "w4a16_moe_gate_up": (ctypes.c_int, [P, P, I32, I32, P, P, I32, P, P, I32, P, P, P, SZ, P]),
+    "w4a16_moe_prepare_x": (ctypes.c_int, [P, P, I32, I32, P, I32, P, SZ, P]),
+    "w4a16_moe_gate_up": (ctypes.c_int, [P, P, I32, I32, P, I32, P, P, I32, P, P, P, SZ, P]),
+    "w4a16_moe_prepare_h": (ctypes.c_int, [P, I32, I32, P, P, I32, P, I32, P, SZ, P]),
     "w4a16_moe_down": (ctypes.c_int, [P, I32, I32, P, P, I32, P, P, I32, P, P, P, SZ, P]),
     "w4a16_moe_combine": (ctypes.c_int, [P, I32, I32, P, P, P, P, P]),
 }

@@ -142,11 +142,14 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
 size_t w4a16_moe_stage_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m) {
   if (check_shape(shape) != W4A16_OK) return 0;
   if (check_tokens(T, topk, shape->num_experts, block_m) != W4A16_OK) return 0;
-  if (block_m != 128) return 0;
+  const int32_t H = shape->hidden, I = shape->intermediate;
   // the tiled path's fp16 A rows: x rows for gate_up, aligned h rows for down
-  // (the two stages run one after the other and share the region)
+  // (the two GEMMs run one after the other and share the region)
   const size_t cap = moe_align_capacity(T, topk, shape->num_experts, block_m);
-  return round_up(std::max(tiled_scratch_bytes(T, shape->hidden), tiled_scratch_bytes((int64_t)cap, shape->intermediate)));
+  size_t need = 0;
+  if (tiled_gemm_supported(block_m, 2 * I, H)) need = std::max(need, tiled_scratch_bytes(T, H));
+  if (tiled_gemm_supported(block_m, H, I)) need = std::max(need, tiled_scratch_bytes((int64_t)cap, I));
+  return round_up(need);
 }
 
 size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m) {
@@ -157,29 +160,70 @@ size_t w4a16_moe_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_
          w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
 }
 
-int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
-                      const int32_t* topk_ids, const int32_t* sorted_token_ids, int32_t capacity,
-                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int32_t block_m,
-                      const void* w13_packed, uint16_t* h, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+int check_stage_workspace(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m, const void* ws,
+                          size_t ws_bytes) {
+  const size_t need = w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
+  return (need > 0 && (!ws || ws_bytes < need)) ? W4A16_ERR_WORKSPACE : W4A16_OK;
+}
+}  // namespace
+
+int w4a16_moe_prepare_x(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                        const int32_t* topk_ids, int32_t block_m, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int st = check_shape(shape);
   if (st != W4A16_OK) return st;
   st = check_tokens(T, topk, shape->num_experts, block_m);
   if (st != W4A16_OK) return st;
-  if ((T > 0 && (!x || !topk_ids)) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w13_packed ||
-      !h)
+  if (T > 0 && (!x || !topk_ids)) return W4A16_ERR_INVALID_ARG;
+  st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
+  if (st != W4A16_OK) return st;
+  if (!tiled_gemm_supported(block_m, 2 * shape->intermediate, shape->hidden)) return W4A16_OK;  // nothing to prepare
+  return hip_status(launch_rows_to_f16_tokens(x, T, shape->hidden, topk_ids, topk, shape->num_experts, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                      const int32_t* sorted_token_ids, int32_t capacity, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int32_t block_m, const void* w13_packed, uint16_t* h,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  st = check_tokens(T, topk, shape->num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if ((T > 0 && !x) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w13_packed || !h)
     return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
-  const size_t need = w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
+  st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
+  if (st != W4A16_OK) return st;
   const int32_t H = shape->hidden, I = shape->intermediate;
   GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded,
                              w13_packed, 2 * I, H);
   p.a = x;
-  p.topk_ids = topk_ids;
   p.out = h;
   p.out_ld = I;
   return hip_status(launch_moe_gemm(kGateUp, block_m, p, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_moe_prepare_h(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
+                        const int32_t* sorted_token_ids, int32_t capacity, const int32_t* num_tokens_post_padded,
+                        int32_t block_m, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  st = check_tokens(T, topk, shape->num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if (!h || !sorted_token_ids || !num_tokens_post_padded) return W4A16_ERR_INVALID_ARG;
+  if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
+    return W4A16_ERR_CAPACITY;
+  st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
+  if (st != W4A16_OK) return st;
+  if (!tiled_gemm_supported(block_m, shape->hidden, shape->intermediate)) return W4A16_OK;  // nothing to prepare
+  // rows past moe_align_capacity are never live (num_tokens_post_padded <= it)
+  const int32_t cap_min = (int32_t)moe_align_capacity(T, topk, shape->num_experts, block_m);
+  return hip_status(launch_rows_to_f16_aligned(h, cap_min, shape->intermediate, sorted_token_ids,
+                                               num_tokens_post_padded, T * topk, workspace,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const uint16_t* h,
@@ -194,12 +238,11 @@ int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const 
     return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
-  // the tiled path converts rows [0, capacity) of h; the scratch is sized for
-  // moe_align_capacity rows, so a larger capacity is clamped to it (rows past
-  // it are never live: num_tokens_post_padded <= moe_align_capacity)
+  st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
+  if (st != W4A16_OK) return st;
+  // the tiled path's prepared rows cover moe_align_capacity rows; rows past it
+  // are never live, so the GEMM is given that capacity
   const size_t cap_min = moe_align_capacity(T, topk, shape->num_experts, block_m);
-  const size_t need = w4a16_moe_stage_workspace_bytes(shape, T, topk, block_m);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
   const int32_t H = shape->hidden, I = shape->intermediate;
   GemmParams p = gemm_params(shape, T, topk, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
                              w2_packed, H, I);
@@ -248,8 +291,13 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
   void* scratch = ws + h_bytes + y_bytes;
   const size_t scratch_bytes = workspace_bytes - h_bytes - y_bytes;
   // Rows past cap_min are never live: num_tokens_post_padded <= cap_min.
-  st = w4a16_moe_gate_up(shape, x, T, topk, topk_ids, sorted_token_ids, (int32_t)cap_min, expert_ids,
-                         num_tokens_post_padded, block_m, w13_packed, h, scratch, scratch_bytes, stream);
+  st = w4a16_moe_prepare_x(shape, x, T, topk, topk_ids, block_m, scratch, scratch_bytes, stream);
+  if (st != W4A16_OK) return st;
+  st = w4a16_moe_gate_up(shape, x, T, topk, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
+                         block_m, w13_packed, h, scratch, scratch_bytes, stream);
+  if (st != W4A16_OK) return st;
+  st = w4a16_moe_prepare_h(shape, T, topk, h, sorted_token_ids, (int32_t)cap_min, num_tokens_post_padded, block_m,
+                           scratch, scratch_bytes, stream);
   if (st != W4A16_OK) return st;
   st = w4a16_moe_down(shape, T, topk, h, sorted_token_ids, (int32_t)cap_min, expert_ids, num_tokens_post_padded,
                       block_m, w2_packed, y, scratch, scratch_bytes, stream);

@@ -67,7 +67,6 @@ struct GemmParams {
   const int32_t* col_exp;  // channel exponents E_n [E, N] (tiled path)
   const int32_t* row_exp;  // A row exponents (tiled path, set by its launcher)
   const uint16_t* a16;     // fp16 copy of the A rows (tiled path, set by its launcher)
-  const int32_t* topk_ids; // [T, topk] (gate_up on the tiled path)
   const int32_t* sorted;   // sorted_token_ids [capacity]
   const int32_t* expert_ids;
   const int32_t* ntpp;     // num_tokens_post_padded (device)
@@ -97,11 +96,17 @@ hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t
 hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, void* scratch, hipStream_t stream);
 
 // Tiled (LDS-staged, 128 x 256 tile, fp16 operands) variant for block_m == 128;
-// used by launch_moe_gemm when the shape fits it. It first converts the A rows
-// it reads to fp16 (with a power-of-two factor per row) into `scratch`, which
-// must hold tiled_scratch_bytes(rows, K): rows = T for gate_up, capacity for down.
-bool tiled_gemm_supported(int32_t block_m, const GemmParams& p);
+// used by launch_moe_gemm when the shape fits it. Its A operand is an fp16 copy
+// of the activation rows with a power-of-two exponent per row, written into
+// `scratch` (tiled_scratch_bytes(rows, K)) beforehand: by
+// launch_rows_to_f16_tokens for gate_up (rows = T, token rows with a resident
+// slot) and launch_rows_to_f16_aligned for down (rows = capacity, real aligned rows).
+bool tiled_gemm_supported(int32_t block_m, int32_t N, int32_t K);
 size_t tiled_scratch_bytes(int64_t rows, int32_t K);
+hipError_t launch_rows_to_f16_tokens(const uint16_t* x, int32_t T, int32_t K, const int32_t* topk_ids, int32_t topk,
+                                     int32_t E, void* scratch, hipStream_t stream);
+hipError_t launch_rows_to_f16_aligned(const uint16_t* h, int32_t capacity, int32_t K, const int32_t* sorted,
+                                      const int32_t* ntpp, int32_t n_slots, void* scratch, hipStream_t stream);
 hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, void* scratch, hipStream_t stream);
 
 // Weight-streaming variant for block_m 16..64 with LDS rings for A and scales;

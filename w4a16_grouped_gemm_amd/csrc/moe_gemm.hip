@@ -319,7 +319,7 @@ int device_cu_count() {
 }
 
 hipError_t launch_moe_gemm(GemmMode mode, int32_t block_m, const GemmParams& p, void* scratch, hipStream_t stream) {
-  if (tiled_gemm_supported(block_m, p)) return launch_moe_gemm_tiled(mode, p, scratch, stream);
+  if (tiled_gemm_supported(block_m, p.N, p.K)) return launch_moe_gemm_tiled(mode, p, scratch, stream);
   if (stream_lds_supported(block_m, p)) return launch_moe_gemm_stream_lds(mode, block_m, p, stream);
   return mode == kGateUp ? launch_mode<kGateUp>(block_m, p, stream) : launch_mode<kDown>(block_m, p, stream);
 }

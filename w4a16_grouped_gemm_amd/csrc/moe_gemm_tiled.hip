@@ -319,6 +319,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
 // the fp16 subnormal grid, an error below 2^-39 of the row's largest element).
 // dst[r] = src[r] * 2^-row_exp[r]. One workgroup per row; rows that no GEMM
 // reads are skipped: by token (a resident topk id) or by aligned row (real slot).
+constexpr int kRowRegs = 4;
+
 template <bool BY_TOKEN>
 __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ src, int32_t K, int32_t nrows,
                                                           const int32_t* __restrict__ topk_ids, int32_t topk,
@@ -338,12 +340,22 @@ __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __rest
     }
     if (!need) continue;  // uniform: every thread read the same values
     const u32x4* row = reinterpret_cast<const u32x4*>(src + (int64_t)r * K);
+    // one read of the row: up to kRowRegs 16-byte chunks per thread stay in
+    // registers (rows up to 8192 elements); longer rows re-read the rest
+    u32x4 v[kRowRegs];
     // largest |x| as a bf16 bit pattern (sign cleared: integer order = magnitude order)
     uint32_t mx = 0;
-    for (int ch = tid; ch < chunks; ch += 256) {
-      const u32x4 v = row[ch];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) mx = max(mx, max(v[d] & 0x7FFFu, (v[d] >> 16) & 0x7FFFu));
+    for (int i = 0; i < kRowRegs; ++i) {
+      const int ch = tid + 256 * i;
+      v[i] = ch < chunks ? row[ch] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) mx = max(mx, max(v[i][d] & 0x7FFFu, (v[i][d] >> 16) & 0x7FFFu));
+    }
+    for (int ch = tid + 256 * kRowRegs; ch < chunks; ch += 256) {
+      const u32x4 w = row[ch];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) mx = max(mx, max(w[d] & 0x7FFFu, (w[d] >> 16) & 0x7FFFu));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
@@ -357,18 +369,23 @@ __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __rest
     const int e = ex - 14;
     if (tid == 0) row_exp[r] = e;
     u32x4* out = reinterpret_cast<u32x4*>(dst + (int64_t)r * K);
-    for (int ch = tid; ch < chunks; ch += 256) {
-      const u32x4 v = row[ch];
+    const auto convert = [&](u32x4 w) {
       u32x4 o;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(v[d] << 16), -e);
-        const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(v[d] & 0xFFFF0000u), -e);
+        const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(w[d] << 16), -e);
+        const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(w[d] & 0xFFFF0000u), -e);
         const f16x2 h = {(_Float16)lo, (_Float16)hi};
         o[d] = __builtin_bit_cast(uint32_t, h);
       }
-      out[ch] = o;
+      return o;
+    };
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i) {
+      const int ch = tid + 256 * i;
+      if (ch < chunks) out[ch] = convert(v[i]);
     }
+    for (int ch = tid + 256 * kRowRegs; ch < chunks; ch += 256) out[ch] = convert(row[ch]);
   }
 }
 
@@ -399,8 +416,8 @@ hipError_t launch_tiled_mode(const GemmParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool tiled_gemm_supported(int32_t block_m, const GemmParams& p) {
-  return block_m == kTileM && (p.K / kGroup) % kStageGroups == 0 && p.N % (kNBlock * kTileNBlocks) == 0;
+bool tiled_gemm_supported(int32_t block_m, int32_t N, int32_t K) {
+  return block_m == kTileM && (K / kGroup) % kStageGroups == 0 && N % (kNBlock * kTileNBlocks) == 0;
 }
 
 size_t tiled_scratch_bytes(int64_t rows, int32_t K) {
@@ -408,25 +425,37 @@ size_t tiled_scratch_bytes(int64_t rows, int32_t K) {
   return (a + 255) / 256 * 256 + (size_t)rows * 4;
 }
 
+namespace {
+int32_t* row_exp_of(void* scratch, int64_t rows, int32_t K) {
+  return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(scratch) + ((size_t)rows * K * 2 + 255) / 256 * 256);
+}
+int rows_grid(int64_t rows) { return (int)std::max<int64_t>(1, std::min<int64_t>(rows, (int64_t)device_cu_count() * 16)); }
+}  // namespace
+
+hipError_t launch_rows_to_f16_tokens(const uint16_t* x, int32_t T, int32_t K, const int32_t* topk_ids, int32_t topk,
+                                     int32_t E, void* scratch, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_to_f16_kernel<true>, dim3(rows_grid(T)), dim3(256), 0, stream, x, K, T, topk_ids, topk, E,
+                     nullptr, nullptr, 0, static_cast<uint16_t*>(scratch), row_exp_of(scratch, T, K));
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_to_f16_aligned(const uint16_t* h, int32_t capacity, int32_t K, const int32_t* sorted,
+                                      const int32_t* ntpp, int32_t n_slots, void* scratch, hipStream_t stream) {
+  if (capacity == 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_to_f16_kernel<false>, dim3(rows_grid(capacity)), dim3(256), 0, stream, h, K, capacity,
+                     nullptr, 0, 0, sorted, ntpp, n_slots, static_cast<uint16_t*>(scratch),
+                     row_exp_of(scratch, capacity, K));
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, void* scratch, hipStream_t stream) {
-  // scratch: fp16 A rows [rows, K] (256-byte aligned), then int32 row exponents [rows]
+  // scratch holds the fp16 A rows and row exponents written by the matching
+  // launch_rows_to_f16_*: T token rows (gate_up) or capacity aligned rows (down)
   const int64_t rows = mode == kGateUp ? (int64_t)p.n_slots / p.topk : p.capacity;
-  uint16_t* a16 = static_cast<uint16_t*>(scratch);
-  int32_t* rexp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(scratch) + ((size_t)rows * p.K * 2 + 255) / 256 * 256);
-  if (rows > 0) {
-    const int grid = (int)std::min<int64_t>(rows, (int64_t)device_cu_count() * 16);
-    if (mode == kGateUp)
-      hipLaunchKernelGGL(rows_to_f16_kernel<true>, dim3(grid), dim3(256), 0, stream, p.a, p.K, (int32_t)rows,
-                         p.topk_ids, p.topk, p.E, p.sorted, p.ntpp, p.n_slots, a16, rexp);
-    else
-      hipLaunchKernelGGL(rows_to_f16_kernel<false>, dim3(grid), dim3(256), 0, stream, p.a, p.K, (int32_t)rows,
-                         p.topk_ids, p.topk, p.E, p.sorted, p.ntpp, p.n_slots, a16, rexp);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   GemmParams q = p;
-  q.a16 = a16;
-  q.row_exp = rexp;
+  q.a16 = static_cast<const uint16_t*>(scratch);
+  q.row_exp = row_exp_of(scratch, rows, p.K);
   return mode == kGateUp ? launch_tiled_mode<kGateUp>(q, stream) : launch_tiled_mode<kDown>(q, stream);
 }
 
