@@ -9,9 +9,13 @@
 // operands q + 136 on v_mfma_f32_16x16x32_bf16, a -136 * sum(x) correction in
 // the C input, one fp32 FMA per output per 32-wide group for the BF16 scale.
 //
-// Work unit: (row block of block_m rows, four consecutive 64-channel n-blocks)
-// for one 256-thread workgroup; wave w streams n-block 4 ng + w over the whole
-// reduction. Only the weight nibbles are held in registers: a ring of kDepth
+// Work unit: (row block of block_m rows, 4 KN consecutive 64-channel n-blocks)
+// for one 256-thread workgroup; wave w streams n-blocks w KN .. w KN + KN - 1 of
+// the unit, whose packed weights are one contiguous region (n-block-major, then
+// group), so its pipeline runs through KN x K/32 groups without a restart and
+// flushes its accumulators at every n-block boundary. KN > 1 only for short
+// reductions (K/32 groups too few to fill the pipeline, e.g. the down
+// projection of an intermediate-sliced layer). Only the weight nibbles are held in registers: a ring of kDepth
 // batches of U groups, so kDepth - 1 batches (kDepth - 1 KiB x U per wave) are
 // in flight while one is computed. The row block's A fragments (gathered
 // activation rows, shared by the four waves) and each wave's group scales go
@@ -80,6 +84,38 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Stores n-block nb of a unit (row block mb) and clears the accumulators.
+// Element i of a 16x16 tile is row 4 (lane >> 4) + i, column lane & 15; ids
+// yields those rows' sorted_token_ids entries.
+template <int MODE, int RB, typename Ids>
+__device__ __forceinline__ void store_nblock(const GemmParams& p, floatx4 (&acc)[RB][4], const Ids& ids, int mb,
+                                             int nb, int lane) {
+  constexpr int BM = 16 * RB;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int prow = mb * BM + rb * 16 + 4 * (lane >> 4) + i;
+      const int id = ids(rb, i);
+      if ((unsigned)id >= (unsigned)p.n_slots) continue;
+      if (MODE == kGateUp) {
+        __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + (lane & 15);
+        h[0] = (__bf16)silu_mul(acc[rb][0][i], acc[rb][2][i]);
+        h[16] = (__bf16)silu_mul(acc[rb][1][i], acc[rb][3][i]);
+      } else {
+        float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + nb * kNBlock + (lane & 15);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[16 * c] = acc[rb][c][i];
+      }
+    }
+  }
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[rb][c] = zero4;
+}
+
 template <int RB, int U, int DEPTH>
 struct Cfg {
   static constexpr int kABlocks = RB * U;                 // 1 KiB A fragments per batch
@@ -88,7 +124,8 @@ struct Cfg {
   static constexpr int kOpsPerBatch = kACopiesPerWave + kSCopies + U;
   static constexpr int kABatchBytes = kABlocks * 1024;
   static constexpr int kSBatchBytes = U * kScaleUnitElems * 2;
-  static constexpr int kLdsBytes = DEPTH * kABatchBytes + 4 * DEPTH * kSBatchBytes;
+  static constexpr int kIdsBytes = 16 * RB * 4;  // the row block's sorted_token_ids
+  static constexpr int kLdsBytes = DEPTH * kABatchBytes + 4 * DEPTH * kSBatchBytes + kIdsBytes;
   static_assert(kABlocks % 4 == 0 && U % 2 == 0, "batch shape");
   static_assert(kOpsPerBatch * (DEPTH - 2) < 64, "vmcnt range");
 };
@@ -96,18 +133,23 @@ struct Cfg {
 // Issue batch b (groups b U .. b U + U - 1) into ring slot `slot`: this wave's
 // A fragment copies, its scale copies, then its nibble loads (in that order,
 // so a wait for the nibbles also covers the copies).
+// a_slot < 0: the A fragments of this batch are already resident (short K,
+// see the kernel); otherwise they are copied into A slot a_slot.
 template <int RB, int U, int DEPTH>
-__device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int b, int wave,
+__device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int a_slot, int b, int G, int wave,
                                             const uint8_t* const* a_src,
                                             const uint8_t* ws, const uint8_t* wq, uint8_t* a_ring, uint8_t* s_ring) {
   using C = Cfg<RB, U, DEPTH>;
   int g0 = b * U;
   asm volatile("" : "+s"(g0));  // keep the look-ahead where it is written
+  const int ga = g0 % G;        // the A rows cycle through K once per n-block
+  if (a_slot >= 0) {
 #pragma unroll
-  for (int t = 0; t < C::kACopiesPerWave; ++t) {
-    const int j = wave + 4 * t;
-    __builtin_amdgcn_global_load_lds(a_src[t] + (int64_t)g0 * (kGroup * 2),
-                                     LDS_PTR(a_ring + slot * C::kABatchBytes + j * 1024), 16, 0, 0);
+    for (int t = 0; t < C::kACopiesPerWave; ++t) {
+      const int j = wave + 4 * t;
+      __builtin_amdgcn_global_load_lds(a_src[t] + (int64_t)ga * (kGroup * 2),
+                                       LDS_PTR(a_ring + a_slot * C::kABatchBytes + j * 1024), 16, 0, 0);
+    }
   }
 #pragma unroll
   for (int t = 0; t < C::kSCopies; ++t)
@@ -118,8 +160,13 @@ __device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int b, in
     nib[uu] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wq + (int64_t)(g0 + uu) * kNibUnitBytes));
 }
 
-template <int MODE, int RB, int U, int DEPTH>
-__global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p) {
+// MULTI: KN > 1 (n-block boundaries inside the batch loop); otherwise KN == 1
+// and the single n-block is stored after the loop, which keeps the common
+// long-K kernel's register count where it was. With MULTI and K / 32 <= U x DEPTH
+// groups the row block's A fragments for the whole of K fit the A ring: they
+// are copied during the first n-block only and stay resident for the others.
+template <int MODE, int RB, int U, int DEPTH, bool MULTI>
+__global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p, int KN) {
   using C = Cfg<RB, U, DEPTH>;
   constexpr int BM = 16 * RB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -127,13 +174,16 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   uint8_t* a_ring = lds;
   uint8_t* s_ring = lds + DEPTH * C::kABatchBytes + wave * DEPTH * C::kSBatchBytes;
+  int* row_ids = reinterpret_cast<int*>(lds + DEPTH * C::kABatchBytes + 4 * DEPTH * C::kSBatchBytes);
 
   const int ntpp = min(*p.ntpp, p.capacity);
   const int n_mblocks = ntpp / BM;
   const int NB = p.N / kNBlock;
-  const int NG = NB / kUnitNBlocks;
+  const int NG = NB / (kUnitNBlocks * KN);  // units per row block
   const int G = p.K / kGroup;
-  const int nbatch = G / U;
+  const int nbatch = KN * G / U;            // batches per wave per unit
+  const int kbatch = G / U;                 // batches per n-block
+  const bool a_resident = MULTI && kbatch <= DEPTH;
   const int units = n_mblocks * NG;
   const int per_wg = (units + (int)gridDim.x - 1) / (int)gridDim.x;
   const int u_begin = (int)blockIdx.x * per_wg;
@@ -148,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
     const int ng = unit - mb * NG;
     const int e = p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
-    const int nb = ng * kUnitNBlocks + wave;
+    const int nb0 = (ng * kUnitNBlocks + wave) * KN;  // this wave's first n-block
 
     // A copy sources: this wave copies fragment blocks j = wave + 4 t of each
     // batch, block j = (row block j / U, group j % U). Padding rows read the
@@ -170,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
       }
       a_src[t] = reinterpret_cast<const uint8_t*>(p.a + src * p.K) + 16 * (lane >> 4) + uu * (kGroup * 2);
     }
-    const int64_t unit0 = ((int64_t)e * NB + nb) * G;
+    const int64_t unit0 = ((int64_t)e * NB + nb0) * G;
     const uint8_t* wq = p.wq + unit0 * kNibUnitBytes + 16 * lane;
     const uint8_t* ws = reinterpret_cast<const uint8_t*>(p.ws + unit0 * kScaleUnitElems) + 4 * lane;
 
@@ -182,22 +232,42 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
 
     u32x4 nib[DEPTH][U];
     ring_barrier();  // the previous unit's reads of every slot are done
+    if (MULTI) {
+      // Stores inside the weight stream read the row ids from LDS: a global
+      // load there would make the wave wait for every batch in flight.
+      if (threadIdx.x < BM) row_ids[threadIdx.x] = p.sorted[mb * BM + threadIdx.x];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible after the next barrier
+    }
+    const auto lds_ids = [&](int rb, int i) { return row_ids[rb * 16 + 4 * (lane >> 4) + i]; };
+    const auto mem_ids = [&](int rb, int i) { return p.sorted[mb * BM + rb * 16 + 4 * (lane >> 4) + i]; };
 #pragma unroll
     for (int s = 0; s < DEPTH - 1; ++s)
-      if (s < nbatch) issue_batch<RB, U, DEPTH>(nib[s], s, s, wave, a_src, ws, wq, a_ring, s_ring);
+      if (s < nbatch)
+        issue_batch<RB, U, DEPTH>(nib[s], s, a_resident ? (s < kbatch ? s : -1) : s, s, G, wave, a_src, ws, wq,
+                                  a_ring, s_ring);
 
     for (int b0 = 0; b0 < nbatch; b0 += DEPTH) {
 #pragma unroll
       for (int k = 0; k < DEPTH; ++k) {
         const int b = b0 + k;
         if (b < nbatch) {
-          if (b + DEPTH - 2 < nbatch) wait_vmcnt<C::kOpsPerBatch * (DEPTH - 2)>();
-          else wait_vmcnt<0>();
+          // own copies and loads of batch b landed (later ones may be pending;
+          // with resident A, later batches may hold fewer ops, so count without
+          // A copies: that waits for at least as much as needed) ...
+          if (b + DEPTH - 2 < nbatch) {
+            if (MULTI) wait_vmcnt<(C::kOpsPerBatch - C::kACopiesPerWave) * (DEPTH - 2)>();
+            else wait_vmcnt<C::kOpsPerBatch * (DEPTH - 2)>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          // ... and everyone's; everyone also finished computing batch b - 1
           ring_barrier();
-          if (b + DEPTH - 1 < nbatch)
-            issue_batch<RB, U, DEPTH>(nib[(k + DEPTH - 1) % DEPTH], (k + DEPTH - 1) % DEPTH, b + DEPTH - 1, wave,
-                                      a_src, ws, wq, a_ring, s_ring);
-          const uint8_t* abase = a_ring + k * C::kABatchBytes;
+          if (b + DEPTH - 1 < nbatch) {
+            const int bn = b + DEPTH - 1, sn = (k + DEPTH - 1) % DEPTH;
+            issue_batch<RB, U, DEPTH>(nib[sn], sn, a_resident ? (bn < kbatch ? bn : -1) : sn, bn, G, wave, a_src, ws,
+                                      wq, a_ring, s_ring);
+          }
+          const uint8_t* abase = a_ring + (a_resident ? b % kbatch : k) * C::kABatchBytes;
           const uint8_t* sbase = s_ring + k * C::kSBatchBytes;
 #pragma unroll
           for (int uu = 0; uu < U; ++uu) {
@@ -215,44 +285,39 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
               for (int c = 0; c < 4; ++c) acc[rb][c] += scale[c] * mfma16(a, w[c], corr);
             }
           }
+          // the last batch of an n-block: store it (uniform branch)
+          if (MULTI && ((b + 1) * U) % G == 0) store_nblock<MODE, RB>(p, acc, lds_ids, mb, nb0 + ((b + 1) * U) / G - 1, lane);
         }
       }
     }
-
-    // Epilogue: element i of a 16x16 tile is row 4 (lane >> 4) + i, column lane & 15.
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int prow = mb * BM + rb * 16 + 4 * (lane >> 4) + i;
-        const int id = p.sorted[prow];
-        if ((unsigned)id >= (unsigned)p.n_slots) continue;
-        if (MODE == kGateUp) {
-          __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + (lane & 15);
-          h[0] = (__bf16)silu_mul(acc[rb][0][i], acc[rb][2][i]);
-          h[16] = (__bf16)silu_mul(acc[rb][1][i], acc[rb][3][i]);
-        } else {
-          float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + nb * kNBlock + (lane & 15);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) y[16 * c] = acc[rb][c][i];
-        }
-      }
-    }
+    if (!MULTI) store_nblock<MODE, RB>(p, acc, mem_ids, mb, nb0, lane);
   }
 }
 
-template <int MODE, int RB, int U, int DEPTH>
-hipError_t launch(const GemmParams& p, hipStream_t stream) {
+// n-blocks per wave: enough for about kMinGroupsPerWave groups of pipeline per
+// unit when K is short, a divisor of the n-blocks per wave lane so units tile N.
+constexpr int kMinGroupsPerWave = 64;
+int n_blocks_per_wave(const GemmParams& p) {
+  const int G = p.K / kGroup;
+  const int NG = p.N / (kNBlock * kUnitNBlocks);
+  int kn = 1;
+  for (int k = 1; k <= NG && (k - 1) * G < kMinGroupsPerWave; ++k)
+    if (NG % k == 0) kn = k;
+  return kn;
+}
+
+template <int MODE, int RB, int U, int DEPTH, bool MULTI>
+hipError_t launch_kn(const GemmParams& p, int kn, hipStream_t stream) {
   using C = Cfg<RB, U, DEPTH>;
   constexpr int BM = 16 * RB;
-  const int64_t units_max = (int64_t)(p.capacity / BM) * (p.N / (kNBlock * kUnitNBlocks));
+  const int64_t units_max = (int64_t)(p.capacity / BM) * (p.N / (kNBlock * kUnitNBlocks * kn));
   if (units_max == 0) return hipSuccess;
   static int blocks_per_cu = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>, kThreads,
-                                                     C::kLdsBytes) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI>,
+                                                     kThreads, C::kLdsBytes) != hipSuccess ||
         n < 1)
       n = 1;
     return n;
@@ -262,9 +327,16 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
   // resident workgroup restarting its pipeline for a second unit (measured
   // faster for the decode down projection).
   const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu * 4);
-  hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH>), dim3((int)grid), dim3(kThreads), C::kLdsBytes,
-                     stream, p);
+  hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI>), dim3((int)grid), dim3(kThreads),
+                     C::kLdsBytes, stream, p, kn);
   return hipGetLastError();
+}
+
+template <int MODE, int RB, int U, int DEPTH>
+hipError_t launch(const GemmParams& p, hipStream_t stream) {
+  const int kn = n_blocks_per_wave(p);
+  return kn == 1 ? launch_kn<MODE, RB, U, DEPTH, false>(p, 1, stream)
+                 : launch_kn<MODE, RB, U, DEPTH, true>(p, kn, stream);
 }
 
 template <int MODE>
