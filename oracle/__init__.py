@@ -49,6 +49,8 @@ def _load():
         lib.oracle_moe_layer.restype = None
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_double
+        lib.oracle_route_topk.argtypes = [P, P, i32, i32, i32, P, P]
+        lib.oracle_route_topk.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         _lib = lib
@@ -87,6 +89,20 @@ def moe_align(topk_ids, E: int, block_m: int, capacity: int | None = None):
     if rc != 0:
         raise ValueError("capacity too small for the alignment")
     return sorted_ids, expert_ids, int(ntpp[0]), counts
+
+
+def route_topk(logits, topk: int, bias=None):
+    """Router: (ids int32 [T, topk], weights fp64 [T, topk]) from fp32 logits [T, Eg]
+    and an optional fp32 bias [Eg]; see oracle_route_topk for the definition."""
+    lg = _c(logits, np.float32)
+    T, Eg = lg.shape
+    b = None if bias is None else _c(bias, np.float32)
+    ids = np.empty((T, topk), np.int32)
+    w = np.empty((T, topk), np.float64)
+    rc = _load().oracle_route_topk(_ptr(lg), None if b is None else _ptr(b), T, Eg, topk, _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError("topk must be in [1, number of experts]")
+    return ids, w
 
 
 def dequant(q, s, N: int, K: int) -> np.ndarray:

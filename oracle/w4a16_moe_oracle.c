@@ -36,6 +36,16 @@
  *    (W4A16 = INT4 weights, BF16 activations, Chord page TL;DR). The per-slot
  *    outputs y stay unrounded.
  *
+ *  - route_topk: the router in front of the alignment, fused with it on the
+ *    FlashInfer Kimi-K3 page (same section: the kernel takes logits and a bias
+ *    and writes topk_weights and topk_ids next to the alignment buffers; its
+ *    1-token cell ranks the winners of every token). The page does not define
+ *    the scoring; this oracle takes the plain reading: the score of expert e is
+ *    the fp32 sum logit + bias[e] (no bias: the logit), the top k scores are
+ *    taken in a stable descending order (equal scores: lower id first), and the
+ *    weights are the softmax over the k chosen raw logits (the bias steers the
+ *    choice only). The weights are computed in fp64.
+ *
  * Parity pins for every function here live in tests/test_oracle_*.py: brute
  * force on tiny inputs, closed forms (permutation / constant / zero weights,
  * one-hot routing), invariants (scale doubling, expert-slice and
@@ -202,6 +212,46 @@ void oracle_moe_layer(const uint16_t* x, int T, int H, int I, int E, int topk,
     }
     free(g); free(h); free(xt);
   }
+}
+
+/* Router: ids [T, topk] and weights [T, topk] (fp64) from logits [T, Eg]
+ * (fp32) and an optional bias [Eg] (fp32, NULL = none). Selection on the fp32
+ * score logit + bias, largest first, equal scores by lower id; weights =
+ * softmax over the chosen raw logits, in fp64. Returns 0, or -1 if topk is
+ * not in [1, Eg]. */
+int oracle_route_topk(const float* logits, const float* bias, int T, int Eg, int topk, int32_t* ids,
+                      double* weights) {
+  if (topk < 1 || topk > Eg) return -1;
+  char* taken = (char*)malloc((size_t)Eg);
+  for (int t = 0; t < T; ++t) {
+    const float* lg = logits + (size_t)t * Eg;
+    memset(taken, 0, (size_t)Eg);
+    for (int j = 0; j < topk; ++j) {
+      int best = -1;
+      float best_score = 0.0f;
+      for (int e = 0; e < Eg; ++e) {
+        if (taken[e]) continue;
+        const float score = bias ? lg[e] + bias[e] : lg[e];
+        if (best < 0 || score > best_score) {  /* strict: an equal score keeps the lower id */
+          best = e;
+          best_score = score;
+        }
+      }
+      taken[best] = 1;
+      ids[(size_t)t * topk + j] = best;
+    }
+    double mx = -INFINITY;
+    for (int j = 0; j < topk; ++j) {
+      const double v = lg[ids[(size_t)t * topk + j]];
+      if (v > mx) mx = v;
+    }
+    double sum = 0.0;
+    for (int j = 0; j < topk; ++j) sum += exp((double)lg[ids[(size_t)t * topk + j]] - mx);
+    for (int j = 0; j < topk; ++j)
+      weights[(size_t)t * topk + j] = exp((double)lg[ids[(size_t)t * topk + j]] - mx) / sum;
+  }
+  free(taken);
+  return 0;
 }
 
 /* Number of OpenMP threads the layer would use (for reporting). */
