@@ -112,6 +112,38 @@ def stored_traffic(workload: str, kernel: str, launches_per_step: int = 1):
     return d.get("hbm_bytes_per_launch")
 
 
+def route_align_timing(w, synthetic, dev, c, bm, reps: int = 50):
+    """Median µs of moe_route_align (top-k routing of fp32 logits over the global experts, then the
+    alignment over the local slice) for one token and for the workload's T tokens, logits warm in L2.
+    Not part of the layer step: the layer takes routed ids as input."""
+    import torch
+
+    Eg = c.meta.get("E_global", c.E)
+    lg = dev(synthetic.router_logits(c.T, Eg, 7))
+    ids = torch.empty((c.T, c.topk), dtype=torch.int32, device="cuda")
+    wts = torch.empty((c.T, c.topk), dtype=torch.float32, device="cuda")
+    buf = w.align_buffers(c.T, c.topk, c.E, bm)
+    out = {}
+    for n in sorted({1, c.T}):
+        def call():
+            w.moe_route_align(lg[:n], c.topk, c.E, bm, ids[:n], wts[:n], buf["sorted_token_ids"], buf["expert_ids"],
+                              buf["num_tokens_post_padded"], workspace=buf["workspace"])
+        for _ in range(5):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            # a spin kernel keeps the GPU busy while the host queues the call, so the
+            # events bracket GPU time and not the host's launch latency
+            torch.cuda._sleep(200000)
+            ev[2 * i].record()
+            call()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        out[f"T{n}"] = round(float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(reps)])), 2)
+    out["experts_routed"] = Eg
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +152,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--block-m", type=int, default=0, help="0: the tokens-per-expert heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-router", action="store_true", help="skip the router + alignment timing")
     ap.add_argument("--cpu-slots", type=int, default=64, help="resident slots the CPU baseline computes")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--copy-probe", action="store_true",
@@ -237,6 +270,8 @@ def main():
         stage_ev.append(ev)
     torch.cuda.synchronize()
 
+    route_us = route_align_timing(w, synthetic, dev, c, bm) if not args.no_router else None
+
     layer_us = np.array([a.elapsed_time(b) * 1e3 for a, b in layer_ev])
     st = np.array([[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(6)] for ev in stage_ev])
     med = float(np.median(layer_us))
@@ -285,6 +320,7 @@ def main():
         "alg_bytes": work["layer_bytes"],
         "alg_flops": work["layer_flops"],
         "roofline": roof,
+        "route_align_us": route_us,
         "source_hash": kernel_source_hash(),
     }
     if args.copy_probe:

@@ -62,6 +62,7 @@ typedef struct {
 #define W4A16_GROUP_SIZE 32
 #define W4A16_MAX_EXPERTS 512
 #define W4A16_MAX_TOPK 32
+#define W4A16_MAX_ROUTED_EXPERTS 1024
 
 /* Human-readable name of a status code (static string; never NULL). */
 const char* w4a16_status_string(int status);
@@ -136,6 +137,42 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
               int32_t* sorted_token_ids, int32_t capacity, int32_t* expert_ids,
               int32_t* num_tokens_post_padded, int32_t* expert_counts, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/* Router and alignment in one call: the step in front of the layer, with the
+ * outputs of the FlashInfer Kimi-K3 fused router (page "[flashinfer]
+ * FlashInfer, B200 GPU에서 Kimi-K3 MoE 라우터 성능 최적화", section "코드 분석":
+ * logits and bias in; top-k weights and ids, sorted_token_ids, expert_ids,
+ * num_tokens_post_padded and the expert counts out). That page gives the
+ * interface, not the arithmetic; the routing computed here is:
+ *   score[t, e]   = logits[t, e] + bias[e]            (fp32 add; bias may be NULL)
+ *   topk_ids[t]   = the topk experts with the highest scores, in descending
+ *                   score order; an equal score goes to the lower expert id
+ *   topk_weights  = softmax over the chosen raw logits (the bias steers the
+ *                   choice only; weights are fp32, not renormalized further)
+ * and the alignment is exactly moe_align's over the ids just written. As on
+ * the page (section "커널 내부 로직 변경 (추정)"), every counter is set inside
+ * the call, so nothing carries over from a previous call.
+ *
+ *   logits                 device fp32 [T, num_routed_experts], finite (NaN
+ *                          logits give unspecified ids, never an out-of-bounds access)
+ *   bias                   device fp32 [num_routed_experts], finite, or NULL
+ *   num_routed_experts     experts the router chooses among, <= W4A16_MAX_ROUTED_EXPERTS;
+ *                          the local slice is ids [0, num_experts) of them
+ *   topk                   1 <= topk <= min(num_routed_experts, W4A16_MAX_TOPK)
+ *   num_experts            local experts, <= num_routed_experts
+ *   topk_ids               device int32 [T, topk], written (global ids)
+ *   topk_weights           device fp32 [T, topk], written
+ *   sorted_token_ids ...   as for moe_align (same capacity rule, same workspace:
+ *   workspace              >= moe_align_workspace_bytes(T, topk, num_experts, block_m))
+ * Returns W4A16_ERR_INVALID_ARG for num_routed_experts < num_experts or
+ * topk > num_routed_experts, W4A16_ERR_UNSUPPORTED past the limits, and the
+ * moe_align codes otherwise. T <= 16 runs as one launch; larger T as a router
+ * launch followed by the alignment launches. Deterministic. */
+int moe_route_align(const float* logits, const float* bias, int32_t T, int32_t num_routed_experts, int32_t topk,
+                    int32_t num_experts, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                    int32_t* sorted_token_ids, int32_t capacity, int32_t* expert_ids,
+                    int32_t* num_tokens_post_padded, int32_t* expert_counts, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* The layer                                                                 */

@@ -95,6 +95,13 @@ def make_x(T: int, H: int, seed: int) -> np.ndarray:
     return to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
 
 
+def router_logits(T: int, E_global: int, seed: int, ties: bool = False) -> np.ndarray:
+    """fp32 N(0, 1) router logits [T, E_global]; ties=True rounds them to multiples
+    of 1/2 so that equal scores are common (the tie-break is then exercised)."""
+    lg = np.random.default_rng(seed).standard_normal((T, E_global), dtype=np.float32)
+    return (np.round(lg * 2) / 2).astype(np.float32) if ties else lg
+
+
 def random_case(name, T, H, I, E, topk, block_m, seed, E_global=None, logit_bias=None, weights=True) -> MoECase:
     """Generic case: N(0,1) logits over E_global experts (default E), local slice [0, E).
 

@@ -102,6 +102,21 @@ def test_validation_status_codes(lib):
     assert lib.moe_align(None, 4, 2, 8, 16, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 1
     cap = w.moe_align_capacity(16384, 8, 48, 128)
     assert lib.moe_align(FAKE, 16384, 8, 48, 128, FAKE, cap, FAKE, FAKE, None, None, 0, None) == 4
+    # router + alignment: (logits, bias, T, Eg, topk, E, block_m, ids, weights, sorted, cap, expert_ids, ntpp,
+    # counts, workspace, workspace_bytes, stream)
+    def ra(T=4, Eg=64, topk=2, E=8, bm=16, logits=FAKE, cap=1000, ws=None, wsb=0):
+        return lib.moe_route_align(logits, None, T, Eg, topk, E, bm, FAKE, FAKE, FAKE, cap, FAKE, FAKE, None, ws,
+                                   wsb, None)
+    assert ra(Eg=4) == 1                                     # fewer routed experts than local ones
+    assert ra(Eg=64, topk=33) == 2                            # topk above the maximum of 32
+    assert ra(Eg=8, topk=9, E=4) == 1                         # topk > routed experts
+    assert ra(Eg=1025) == 2                                   # routed experts above the maximum
+    assert ra(logits=None) == 1
+    assert ra(bm=8) == 2
+    assert ra(cap=w.moe_align_capacity(4, 2, 8, 16) - 1) == 3
+    cap = w.moe_align_capacity(16384, 8, 48, 128)
+    assert ra(T=16384, Eg=384, topk=8, E=48, bm=128, cap=cap) == 4
+    assert ra(T=16384, Eg=384, topk=8, E=48, bm=128, cap=cap, ws=FAKE, wsb=16) == 4
     # repack and stages
     assert lib.w4a16_repack(ctypes.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1

@@ -14,6 +14,7 @@ from ._lib import LIB_PATH, Shape, load
 __all__ = [
     "W4A16Error", "Shape", "LIB_PATH", "load", "make_shape", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "moe_align_capacity", "moe_align_workspace_bytes", "w4a16_choose_block_m", "moe_align",
+    "moe_route_align", "w4a16_moe_stage_workspace_bytes", "w4a16_moe_prepare_x", "w4a16_moe_prepare_h",
     "w4a16_moe_workspace_bytes", "w4a16_moe_forward", "w4a16_moe_gate_up", "w4a16_moe_down",
     "w4a16_moe_combine", "align_buffers",
 ]
@@ -83,6 +84,15 @@ def moe_align(topk_ids, num_experts: int, block_m: int, sorted_token_ids, expert
     _check(load().moe_align(_p(topk_ids), T, topk, num_experts, block_m, _p(sorted_token_ids),
                             sorted_token_ids.numel(), _p(expert_ids), _p(num_tokens_post_padded),
                             _p(expert_counts), _p(workspace), nbytes, _stream(stream)), "moe_align")
+
+
+def moe_route_align(logits, topk: int, num_experts: int, block_m: int, topk_ids, topk_weights, sorted_token_ids,
+                    expert_ids, num_tokens_post_padded, bias=None, expert_counts=None, workspace=None, stream=None):
+    T, Eg = logits.shape
+    _check(load().moe_route_align(_p(logits), _p(bias), T, Eg, topk, num_experts, block_m, _p(topk_ids),
+                                  _p(topk_weights), _p(sorted_token_ids), sorted_token_ids.numel(), _p(expert_ids),
+                                  _p(num_tokens_post_padded), _p(expert_counts), _p(workspace), _nbytes(workspace),
+                                  _stream(stream)), "moe_route_align")
 
 
 def w4a16_moe_workspace_bytes(shape: Shape, T: int, topk: int, block_m: int) -> int:

@@ -26,6 +26,7 @@ SIGNATURES = {
     "moe_align_workspace_bytes": (SZ, [I32, I32, I32, I32]),
     "w4a16_choose_block_m": (I32, [I32, I32, I32, I32]),
     "moe_align": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, P, P, P, SZ, P]),
+    "moe_route_align": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P]),
     "w4a16_moe_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_stage_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_forward": (ctypes.c_int, [P, P, I32, I32, P, P, P, I32, P, P, I32, P, P, P, P, SZ, P]),

@@ -180,20 +180,16 @@ __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nb
 }
 
 // ---- single-launch path -----------------------------------------------------
-// LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
-__global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
-                                                               int32_t* __restrict__ sorted, int capacity,
-                                                               int32_t* __restrict__ expert_ids, int nblk,
-                                                               int32_t* __restrict__ ntpp_out,
-                                                               int32_t* __restrict__ counts_out) {
-  extern __shared__ int smem[];
+// The whole alignment of n <= kSmallMax ids held in v (see id_index, lo = 0) by
+// one block. LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
+__device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, int* smem, int32_t* __restrict__ sorted,
+                            int capacity, int32_t* __restrict__ expert_ids, int nblk, int32_t* __restrict__ ntpp_out,
+                            int32_t* __restrict__ counts_out) {
   int* counts = smem;
   int* off = counts + E;
   int* cursor = off + E + 1;
   int* wtab = cursor + E;
-  int v[kPerThread];
   const int steps = block_steps(0, n);
-  load_ids(ids, 0, n, steps, v);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = 0;
   __syncthreads();
   count_ids(v, E, counts);
@@ -210,6 +206,17 @@ __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, (int)threadIdx.x, kThreads);
   __syncthreads();
   scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, 0);
+}
+
+__global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
+                                                               int32_t* __restrict__ sorted, int capacity,
+                                                               int32_t* __restrict__ expert_ids, int nblk,
+                                                               int32_t* __restrict__ ntpp_out,
+                                                               int32_t* __restrict__ counts_out) {
+  extern __shared__ int smem[];
+  int v[kPerThread];
+  load_ids(ids, 0, n, block_steps(0, n), v);
+  align_block(v, n, E, bm, smem, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out);
 }
 
 // ---- multi-block path -------------------------------------------------------
@@ -286,6 +293,174 @@ __global__ void align_empty_kernel(int32_t* sorted, int capacity, int sentinel, 
   if (tid == 0) *ntpp_out = 0;
 }
 
+// ---- router ------------------------------------------------------------------
+// Top-k routing of one token by one wave, the step the FlashInfer Kimi-K3 fused
+// router runs before its alignment (page "[flashinfer] FlashInfer, B200 GPU에서
+// Kimi-K3 MoE 라우터 성능 최적화", sections "코드 분석" and "커널 내부 로직 변경
+// (추정)"). The page shows the router's interface (logits, bias -> top-k
+// weights, ids and the alignment buffers) but not its arithmetic; the
+// definition here: score = logit + bias in fp32, the topk highest scores in
+// descending order with an equal score going to the lower expert id, weights =
+// softmax over the chosen raw logits (the bias steers the choice only).
+//
+// Lane l holds experts l, l + 64, l + 128, ... (coalesced row reads), each
+// score as an order-preserving integer key. Each of the topk rounds is one
+// wave-wide integer max over DPP (quad swaps, row mirrors, row broadcasts: no
+// LDS round trips), then one ballot per expert slot finds the lowest expert
+// holding that key; keys compare exactly as the fp32 scores do, so ties
+// resolve exactly as the definition says.
+
+constexpr int kRouteWaves = 4;  // tokens per block of the stand-alone router
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float v, float old) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
+}
+
+// Wave-wide max / sum, returned to every lane. Steps: quad_perm [1,0,3,2] and
+// [2,3,0,1] (quads), row_half_mirror (8 lanes), row_mirror (16 lanes), then
+// row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3: lane 63
+// ends with the whole wave. Rows a step does not write keep `old` (the
+// operation's identity).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xb1, 0xf>(v, v));
+  v = fmaxf(v, dpp_mov<0x4e, 0xf>(v, v));
+  v = fmaxf(v, dpp_mov<0x141, 0xf>(v, v));
+  v = fmaxf(v, dpp_mov<0x140, 0xf>(v, v));
+  v = fmaxf(v, dpp_mov<0x142, 0xa>(v, v));
+  v = fmaxf(v, dpp_mov<0x143, 0xc>(v, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xb1, 0xf>(v, 0.f);
+  v += dpp_mov<0x4e, 0xf>(v, 0.f);
+  v += dpp_mov<0x141, 0xf>(v, 0.f);
+  v += dpp_mov<0x140, 0xf>(v, 0.f);
+  v += dpp_mov<0x142, 0xa>(v, 0.f);
+  v += dpp_mov<0x143, 0xc>(v, 0.f);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Order-preserving map of a non-NaN float to a uint32 key >= 0x007fffff
+// (-inf); -0 and +0 share one key, as they compare equal. Key 0 marks an
+// expert already chosen (or absent).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (u == 0x80000000u) return 0x80000000u;  // -0 -> key of +0
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Routes token t (the calling wave, all 64 lanes active). Lane j < topk writes
+// topk_ids[t, j] and topk_weights[t, j] and returns the id; other lanes return -1.
+// SLOTS * 64 >= Eg; requires 1 <= topk <= min(Eg, 64).
+template <int SLOTS>
+__device__ int route_token(const float* __restrict__ logits, const float* __restrict__ bias, int t, int Eg, int topk,
+                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
+  const int lane = (int)threadIdx.x & 63;
+  const float* row = logits + (size_t)t * Eg;
+  float raw[SLOTS], b[SLOTS];
+  uint32_t key[SLOTS];
+  // unconditional (clamped) loads, so all of them are in flight at once
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) raw[j] = row[min(lane + 64 * j, Eg - 1)];
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) b[j] = bias[min(lane + 64 * j, Eg - 1)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) b[j] = 0.f;  // x + 0 orders like x
+  }
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) key[j] = lane + 64 * j < Eg ? order_key(raw[j] + b[j]) : 0u;
+  int my_id = -1;
+  float my_logit = -INFINITY;
+  for (int r = 0; r < topk; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int j = 1; j < SLOTS; ++j) best = max(best, key[j]);
+    const uint32_t m = wave_max_u32(best);  // > 0: an open expert remains (topk <= Eg)
+    // lowest expert id holding key m: the first slot with a hit, then its lowest lane
+    int wj = 0, wl = 0;
+#pragma unroll
+    for (int j = SLOTS - 1; j >= 0; --j) {
+      const uint64_t hit = __ballot(key[j] == m);
+      if (hit) {
+        wj = j;
+        wl = (int)__builtin_ctzll(hit);
+      }
+    }
+    float sel = raw[0];
+#pragma unroll
+    for (int j = 1; j < SLOTS; ++j) sel = j == wj ? raw[j] : sel;
+    const float lg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sel), wl));
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) key[j] = (j == wj && lane == wl) ? 0u : key[j];
+    if (lane == r) {
+      my_id = wl + 64 * wj;
+      my_logit = lg;
+    }
+  }
+  const float mx = wave_max(my_logit);  // lanes >= topk hold -inf
+  const float ex = lane < topk ? expf(my_logit - mx) : 0.f;
+  const float sum = wave_sum(ex);
+  if (lane < topk) {
+    topk_ids[(size_t)t * topk + lane] = my_id;
+    topk_weights[(size_t)t * topk + lane] = ex / sum;
+  }
+  return my_id;
+}
+
+// Stand-alone router: one wave per token.
+template <int SLOTS>
+__global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(const float* __restrict__ logits,
+                                                                 const float* __restrict__ bias, int T, int Eg,
+                                                                 int topk, int32_t* __restrict__ topk_ids,
+                                                                 float* __restrict__ topk_weights) {
+  const int t = (int)blockIdx.x * kRouteWaves + ((int)threadIdx.x >> 6);
+  if (t < T) route_token<SLOTS>(logits, bias, t, Eg, topk, topk_ids, topk_weights);
+}
+
+// Router and alignment in one launch for T <= kWaves tokens: wave w routes
+// token w and leaves its ids in LDS, then the block aligns them (every counter
+// is set inside the kernel, nothing is read from a previous call).
+// LDS: ids[kWaves * 32] (32 = the largest topk), then the alignment's tables.
+constexpr int kFusedIds = kWaves * 32;
+
+template <int SLOTS>
+__global__ __launch_bounds__(kThreads) void route_align_small_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int Eg, int topk, int E, int bm,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ sorted, int capacity,
+    int32_t* __restrict__ expert_ids, int nblk, int32_t* __restrict__ ntpp_out, int32_t* __restrict__ counts_out) {
+  extern __shared__ int smem[];
+  int* ids = smem;
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  if (wave < T) {
+    const int id = route_token<SLOTS>(logits, bias, wave, Eg, topk, topk_ids, topk_weights);
+    if (lane < topk) ids[wave * topk + lane] = id;
+  }
+  __syncthreads();
+  const int n = T * topk;
+  int v[kPerThread];
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const int i = id_index(0, 1, r);  // n <= kThreads: one step
+    v[r] = (r == 0 && i < n) ? ids[i] : -1;
+  }
+  align_block(v, n, E, bm, smem + kFusedIds, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out);
+}
+
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t scatter_lds(int E) { return sizeof(int) * (size_t)(3 * E + 1 + kWaves * E); }
@@ -321,6 +496,45 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, in
   hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, hist,
                      nchunks, sorted, capacity, expert_ids, nblk, ntpp, counts);
   return hipGetLastError();
+}
+
+namespace {
+template <int SLOTS>
+hipError_t launch_route_align_slots(const float* logits, const float* bias, int32_t T, int32_t Eg, int32_t topk,
+                                    int32_t E, int32_t bm, int32_t* topk_ids, float* topk_weights, int32_t* sorted,
+                                    int32_t capacity, int32_t* expert_ids, int32_t* ntpp, int32_t* counts,
+                                    void* workspace, hipStream_t stream) {
+  if (T <= kWaves) {
+    const int nblk = (capacity + bm - 1) / bm;
+    hipLaunchKernelGGL(route_align_small_kernel<SLOTS>, dim3(1), dim3(kThreads),
+                       sizeof(int) * kFusedIds + scatter_lds(E), stream, logits, bias, T, Eg, topk, E, bm, topk_ids,
+                       topk_weights, sorted, capacity, expert_ids, nblk, ntpp, counts);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_kernel<SLOTS>, dim3((T + kRouteWaves - 1) / kRouteWaves), dim3(64 * kRouteWaves), 0,
+                     stream, logits, bias, T, Eg, topk, topk_ids, topk_weights);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_align(topk_ids, T * topk, E, bm, sorted, capacity, expert_ids, ntpp, counts, workspace, stream);
+}
+}  // namespace
+
+hipError_t launch_route_align(const float* logits, const float* bias, int32_t T, int32_t Eg, int32_t topk, int32_t E,
+                              int32_t bm, int32_t* topk_ids, float* topk_weights, int32_t* sorted, int32_t capacity,
+                              int32_t* expert_ids, int32_t* ntpp, int32_t* counts, void* workspace,
+                              hipStream_t stream) {
+  if (T == 0) return launch_align(topk_ids, 0, E, bm, sorted, capacity, expert_ids, ntpp, counts, workspace, stream);
+  if (Eg <= 128)
+    return launch_route_align_slots<2>(logits, bias, T, Eg, topk, E, bm, topk_ids, topk_weights, sorted, capacity,
+                                       expert_ids, ntpp, counts, workspace, stream);
+  if (Eg <= 256)
+    return launch_route_align_slots<4>(logits, bias, T, Eg, topk, E, bm, topk_ids, topk_weights, sorted, capacity,
+                                       expert_ids, ntpp, counts, workspace, stream);
+  if (Eg <= 512)
+    return launch_route_align_slots<8>(logits, bias, T, Eg, topk, E, bm, topk_ids, topk_weights, sorted, capacity,
+                                       expert_ids, ntpp, counts, workspace, stream);
+  return launch_route_align_slots<16>(logits, bias, T, Eg, topk, E, bm, topk_ids, topk_weights, sorted, capacity,
+                                      expert_ids, ntpp, counts, workspace, stream);
 }
 
 }  // namespace w4a16

@@ -139,6 +139,25 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
                                  num_tokens_post_padded, expert_counts, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int moe_route_align(const float* logits, const float* bias, int32_t T, int32_t num_routed_experts, int32_t topk,
+                    int32_t num_experts, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                    int32_t* sorted_token_ids, int32_t capacity, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                    int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_tokens(T, topk, num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if (num_routed_experts < num_experts || topk > num_routed_experts) return W4A16_ERR_INVALID_ARG;
+  if (num_routed_experts > W4A16_MAX_ROUTED_EXPERTS) return W4A16_ERR_UNSUPPORTED;
+  if ((T > 0 && (!logits || !topk_ids || !topk_weights)) || !sorted_token_ids || !expert_ids ||
+      !num_tokens_post_padded)
+    return W4A16_ERR_INVALID_ARG;
+  if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, num_experts, block_m)) return W4A16_ERR_CAPACITY;
+  const size_t ws = align_workspace_bytes((int64_t)T * topk, num_experts);
+  if (ws > 0 && (!workspace || workspace_bytes < ws)) return W4A16_ERR_WORKSPACE;
+  return hip_status(launch_route_align(logits, bias, T, num_routed_experts, topk, num_experts, block_m, topk_ids,
+                                       topk_weights, sorted_token_ids, capacity, expert_ids, num_tokens_post_padded,
+                                       expert_counts, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t w4a16_moe_stage_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t block_m) {
   if (check_shape(shape) != W4A16_OK) return 0;
   if (check_tokens(T, topk, shape->num_experts, block_m) != W4A16_OK) return 0;

@@ -88,6 +88,14 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t block_
                         void* workspace, hipStream_t stream);
 size_t align_workspace_bytes(int64_t n, int32_t E);
 
+// Top-k routing of fp32 logits [T, Eg] (+ optional bias [Eg]) into topk_ids /
+// topk_weights, then the alignment of those ids over the local experts [0, E).
+// Eg <= 1024, topk <= min(Eg, 32). Same workspace as launch_align.
+hipError_t launch_route_align(const float* logits, const float* bias, int32_t T, int32_t Eg, int32_t topk, int32_t E,
+                              int32_t block_m, int32_t* topk_ids, float* topk_weights, int32_t* sorted,
+                              int32_t capacity, int32_t* expert_ids, int32_t* ntpp, int32_t* counts, void* workspace,
+                              hipStream_t stream);
+
 // Writes all four regions of one projection's packed buffer.
 hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t N, int32_t K,
                          int32_t interleave_I, uint8_t* packed, hipStream_t stream);
