@@ -13,19 +13,23 @@
 // Design (the work is tiny; the kernels are written against latency):
 //  * every thread loads its ids once, up front, into registers;
 //  * histogram: LDS atomics on per-expert counters (order-free, so deterministic);
-//  * offsets: one wave scans the padded counts with lane shuffles;
+//  * offsets: one wave scans the padded counts with DPP (row shifts and row
+//    broadcasts, no LDS round trips);
 //  * ranking: each wave owns a contiguous segment of ids and ranks it 64 at a
 //    time against its own per-expert counters in LDS (lanes of one expert are
 //    found with one ballot per bit of the expert id; a lane's rank is the
-//    mbcnt of its peers below it); one scan per expert across the 16 waves
-//    gives the bases. Positions depend only on the input, never on timing;
-//  * padding sentinels are written per expert (at most block_m - 1 each), used
-//    blocks are labelled with one search each, and the unused tail is a plain
-//    fill: no per-position search over the over-allocated buffer.
+//    mbcnt of its peers below it); one 16-lane DPP row scan per expert across
+//    the 16 waves gives the bases. Positions depend only on the input, never
+//    on timing;
+//  * each used block is labelled by a 16-lane group (one binary search), which
+//    also writes that block's padding sentinels; the unused tail is a plain
+//    fill: no per-position search over the over-allocated buffer;
+//  * barriers order LDS traffic only; they never wait for global stores.
 // Small inputs run in one block and one launch. Larger ones use two launches:
 // per-chunk histograms, then one block per chunk that recomputes the (small)
 // expert prefix itself from all chunk histograms and scatters its chunk.
 #include "internal.h"
+#include "w4a16_moe.h"
 
 #include <algorithm>
 
@@ -43,7 +47,40 @@ __device__ __forceinline__ int rank_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ int padded(int c, int bm) { return (c + bm - 1) / bm * bm; }
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then s_barrier. Outstanding global stores are not waited for: no thread of
+// these kernels reads what another thread of its block stored to global memory.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// v + the value DPP moves in (0 where the row mask or the row bound leaves none).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum inside each row of 16 lanes (row_shr 1, 2, 4, 8); all
+// 16 lanes of a row must be active.
+__device__ __forceinline__ int row_incl_scan(int v) {
+  v = dpp_add<0x111, 0xf>(v);
+  v = dpp_add<0x112, 0xf>(v);
+  v = dpp_add<0x114, 0xf>(v);
+  return dpp_add<0x118, 0xf>(v);
+}
+
+// Inclusive prefix sum over the wave: row scans, then row 0's total into row 1
+// and row 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2-3
+// (row_bcast:31). All 64 lanes must be active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v = row_incl_scan(v);
+  v = dpp_add<0x142, 0xa>(v);
+  return dpp_add<0x143, 0xc>(v);
+}
+
+__device__ __forceinline__ int padded(int c, int bm) { return (c + bm - 1) & -bm; }  // bm: a power of two
 
 __device__ __forceinline__ int id_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
 
@@ -71,52 +108,78 @@ __device__ __forceinline__ void count_ids(const int (&v)[kPerThread], int E, int
     if ((unsigned)v[r] < (unsigned)E) atomicAdd(&hist[v[r]], 1);
 }
 
-// Wave 0 writes off[0..E] = exclusive prefix of padded counts; off[E] = total.
-__device__ void scan_offsets(const int* counts, int E, int bm, int* off) {
+// Wave 0 writes off[0..E] = exclusive prefix of padded counts (off[E] = the
+// padded total), cursor[e] = off[e] (+ the old cursor[e] when add_cursor), and,
+// where the pointers are not null, the counts and the padded total to global
+// memory. Lane l owns experts [l * per, (l + 1) * per), held in registers; one
+// DPP wave scan. E <= 64 * kMaxExpertsPerLane.
+constexpr int kMaxExpertsPerLane = 8;
+static_assert(64 * kMaxExpertsPerLane >= W4A16_MAX_EXPERTS, "one scan wave must hold every expert");
+
+__device__ void scan_offsets(const int* counts, int E, int bm, int* off, int* cursor, bool add_cursor,
+                             int32_t* __restrict__ counts_out, int32_t* __restrict__ ntpp_out) {
   if (threadIdx.x < 64) {
     const int lane = (int)threadIdx.x;
     const int per = (E + 63) / 64;
     const int start = lane * per;
+    int c[kMaxExpertsPerLane];
     int local = 0;
-    for (int k = 0; k < per; ++k) {
-      const int e = start + k;
-      if (e < E) local += padded(counts[e], bm);
+#pragma unroll
+    for (int k = 0; k < kMaxExpertsPerLane; ++k) {
+      c[k] = (k < per && start + k < E) ? counts[start + k] : 0;
+      local += padded(c[k], bm);
     }
-    int incl = local;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int x = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += x;
-    }
+    const int incl = wave_incl_scan(local);
     int run = incl - local;
-    for (int k = 0; k < per; ++k) {
+#pragma unroll
+    for (int k = 0; k < kMaxExpertsPerLane; ++k) {
       const int e = start + k;
-      if (e < E) {
+      if (k < per && e < E) {
         off[e] = run;
-        run += padded(counts[e], bm);
+        cursor[e] = (add_cursor ? cursor[e] : 0) + run;
+        if (counts_out) counts_out[e] = c[k];
+        run += padded(c[k], bm);
       }
     }
-    if (lane == 63) off[E] = incl;
+    if (lane == 63) {
+      off[E] = incl;
+      if (ntpp_out) *ntpp_out = incl;
+    }
   }
 }
 
-// Largest e in [0, E) with off[e] <= p (requires p < off[E]).
-__device__ __forceinline__ int find_expert(const int* off, int E, int p) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (off[mid] <= p) lo = mid; else hi = mid;
+// Largest e in [0, E) with off[e] <= p (requires p < off[E]), found by the 16
+// lanes of a group (lanes 16 g .. 16 g + 15 of a wave, all active) together:
+// each step tests 16 evenly spaced candidates at once (E = 48: two steps; 512: three).
+__device__ __forceinline__ int find_expert16(const int* off, int E, int p, int sub) {
+  const int shift = (int)threadIdx.x & 48;  // this group's bits in the wave's ballot
+  int lo = 0, span = E;                     // off[lo] <= p; the answer lies in [lo, lo + span)
+  while (span > 1) {
+    const int step = (span + 15) >> 4;
+    const bool ok = sub * step < span && off[lo + sub * step] <= p;
+    const uint32_t bits = (uint32_t)(__ballot(ok) >> shift) & 0xffffu;  // bit 0 set: off[lo] <= p
+    const int k = 31 - __clz(bits);
+    lo += k * step;
+    span = min(step, span - k * step);
   }
   return lo;
 }
 
-// Used blocks get their expert (one search per block, blocks strided from
-// t0); each expert's at most bm - 1 padding slots get the sentinel.
-__device__ void label_experts(const int* off, const int* counts, int E, int bm, int32_t* sorted,
-                              int32_t* expert_ids, int sentinel, int t0, int step) {
-  const int used = off[E] / bm;
-  for (int b = t0; b < used; b += step) expert_ids[b] = find_expert(off, E, b * bm);
-  for (int e = t0; e < E; e += step)
-    for (int p = off[e] + counts[e]; p < off[e + 1]; ++p) sorted[p] = sentinel;
+// Block labels and padding sentinels, one 16-lane group per used block b
+// (groups g0, g0 + gstep, ...): the group finds b's expert by a 16-way search,
+// its lane 0 labels the
+// block and its lanes fill the block's padding slots. Only an expert's last
+// block holds padding (at most block_m - 1 slots).
+__device__ void label_blocks(const int* off, const int* counts, int E, int bm, int32_t* sorted, int32_t* expert_ids,
+                             int nblk, int capacity, int sentinel, int g0, int gstep) {
+  const int used = min(off[E] / bm, nblk);  // == off[E] / bm: capacity covers every padded count
+  const int sub = (int)threadIdx.x & 15;
+  for (int b = g0; b < used; b += gstep) {
+    const int e = find_expert16(off, E, b * bm, sub);
+    if (sub == 0) expert_ids[b] = e;
+    const int end = min((b + 1) * bm, capacity);
+    for (int p = max(b * bm, off[e] + counts[e]) + sub; p < end; p += 16) sorted[p] = sentinel;
+  }
 }
 
 // Unused tail: sorted[ntpp, capacity) = sentinel, expert_ids[ntpp / bm, nblk) = -1.
@@ -132,14 +195,12 @@ __device__ void fill_tail(int ntpp, int bm, int32_t* sorted, int capacity, int32
 // wave-private counter row wcnt[wave][e] in LDS (lanes of one expert in a step
 // are found with one ballot per id bit; the rank is the mbcnt of the peers
 // below), so the steps need no workgroup barrier. The 16 per-wave counts of an
-// expert are then turned into per-wave bases by a 16-lane segmented shuffle
-// scan. wcnt is LDS scratch of kWaves * E ints.
+// expert are then turned into per-wave bases by one 16-lane row scan. wcnt is
+// LDS scratch of kWaves * E ints, zeroed by the caller before its last barrier.
 __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nbits, const int* cursor, int* wcnt,
-                            int32_t* __restrict__ sorted, int lo) {
+                            int32_t* __restrict__ sorted, int capacity, int lo) {
   const int wave = (int)threadIdx.x >> 6;
   int* row = wcnt + wave * E;
-  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wcnt[k] = 0;
-  __syncthreads();
   int rank[kPerThread];
 #pragma unroll
   for (int r = 0; r < kPerThread; ++r) {
@@ -159,24 +220,21 @@ __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nb
       if (local && below == 0) row[e] = prev + __popcll(peers);
     }
   }
-  __syncthreads();  // all waves' counts final
-  // pair (expert x, wave w) at index 16 x + w: 16 consecutive lanes hold one expert
-  // kWaves * E is a multiple of 16, so every 16-lane segment is fully active
+  lds_barrier();  // all waves' counts final
+  // pair (expert x, wave w) at index 16 x + w: one 16-lane row holds one expert;
+  // kWaves * E is a multiple of 16, so every row is fully active
   for (int idx = (int)threadIdx.x; idx < kWaves * E; idx += kThreads) {
     const int x = idx >> 4, w = idx & 15;
     const int c = wcnt[w * E + x];
-    int incl = c;
-#pragma unroll
-    for (int d = 1; d < kWaves; d <<= 1) {
-      const int up = __shfl_up(incl, d, kWaves);
-      if (w >= d) incl += up;
-    }
-    wcnt[w * E + x] = cursor[x] + incl - c;  // only this lane ever touches this entry
+    wcnt[w * E + x] = cursor[x] + row_incl_scan(c) - c;  // only this lane ever touches this entry
   }
-  __syncthreads();  // per-wave bases visible
+  lds_barrier();  // per-wave bases visible
 #pragma unroll
   for (int r = 0; r < kPerThread; ++r)
-    if (r < steps && (unsigned)v[r] < (unsigned)E) sorted[row[v[r]] + rank[r]] = id_index(lo, steps, r);
+    if (r < steps && (unsigned)v[r] < (unsigned)E) {
+      const int pos = row[v[r]] + rank[r];  // < capacity: the capacity covers every padded count
+      if ((unsigned)pos < (unsigned)capacity) sorted[pos] = id_index(lo, steps, r);
+    }
 }
 
 // ---- single-launch path -----------------------------------------------------
@@ -191,21 +249,18 @@ __device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, in
   int* wtab = cursor + E;
   const int steps = block_steps(0, n);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = 0;
-  __syncthreads();
+  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
+  lds_barrier();
   count_ids(v, E, counts);
-  __syncthreads();
-  scan_offsets(counts, E, bm, off);
-  __syncthreads();
+  lds_barrier();
+  scan_offsets(counts, E, bm, off, cursor, false, counts_out, ntpp_out);
+  lds_barrier();
   const int ntpp = off[E];
-  if (threadIdx.x == 0) *ntpp_out = ntpp;
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
-    cursor[e] = off[e];
-    if (counts_out) counts_out[e] = counts[e];
-  }
-  label_experts(off, counts, E, bm, sorted, expert_ids, n, (int)threadIdx.x, kThreads);
+  label_blocks(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, (int)threadIdx.x >> 4,
+               kThreads / 16);
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, (int)threadIdx.x, kThreads);
-  __syncthreads();
-  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, 0);
+  lds_barrier();
+  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, capacity, 0);
 }
 
 __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
@@ -228,9 +283,9 @@ __global__ __launch_bounds__(kThreads) void align_hist_kernel(const int32_t* __r
   const int lo = (int)blockIdx.x * kChunk;
   load_ids(ids, lo, min(n, lo + kChunk), block_steps(lo, min(n, lo + kChunk)), v);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) smem[e] = 0;
-  __syncthreads();
+  lds_barrier();
   count_ids(v, E, smem);
-  __syncthreads();
+  lds_barrier();
   for (int e = (int)threadIdx.x; e < E; e += kThreads) hist[(size_t)blockIdx.x * E + e] = smem[e];
 }
 
@@ -254,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
   const int lo = (int)blockIdx.x * kChunk;
   const int steps = block_steps(lo, min(n, lo + kChunk));
   load_ids(ids, lo, min(n, lo + kChunk), steps, v);
+  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
   for (int e = (int)threadIdx.x; e < E; e += kThreads) {
     int total = 0, before = 0;
 #pragma unroll 8  // independent loads in flight (the histograms sit in L2)
@@ -265,21 +321,16 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
     counts[e] = total;
     cursor[e] = before;  // this chunk's base inside the expert, before adding off[e]
   }
-  __syncthreads();
-  scan_offsets(counts, E, bm, off);
-  __syncthreads();
+  lds_barrier();
+  scan_offsets(counts, E, bm, off, cursor, true, blockIdx.x == 0 ? counts_out : nullptr,
+               blockIdx.x == 0 ? ntpp_out : nullptr);
+  lds_barrier();
   const int ntpp = off[E];
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) cursor[e] += off[e];
-  if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) *ntpp_out = ntpp;
-    for (int e = (int)threadIdx.x; e < E; e += kThreads)
-      if (counts_out) counts_out[e] = counts[e];
-  }
   const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
-  label_experts(off, counts, E, bm, sorted, expert_ids, n, gt, gstep);
+  label_blocks(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, gt >> 4, gstep / 16);
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, gt, gstep);
-  __syncthreads();
-  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, lo);
+  lds_barrier();
+  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, capacity, lo);
 }
 
 // T == 0: every output is a sentinel.
@@ -437,6 +488,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(const float* __
 // is set inside the kernel, nothing is read from a previous call).
 // LDS: ids[kWaves * 32] (32 = the largest topk), then the alignment's tables.
 constexpr int kFusedIds = kWaves * 32;
+static_assert(32 >= W4A16_MAX_TOPK, "fused ids buffer");
 
 template <int SLOTS>
 __global__ __launch_bounds__(kThreads) void route_align_small_kernel(
@@ -450,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void route_align_small_kernel(
     const int id = route_token<SLOTS>(logits, bias, wave, Eg, topk, topk_ids, topk_weights);
     if (lane < topk) ids[wave * topk + lane] = id;
   }
-  __syncthreads();
+  lds_barrier();
   const int n = T * topk;
   int v[kPerThread];
 #pragma unroll
