@@ -38,10 +38,15 @@ BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 fl
 DEFAULT_WORKLOAD = "decode_ep48"
 
 
+# the sources of the GEMM kernels and of the packed weight layout they read: the
+# stored HBM byte counts stay valid while these are unchanged
+GEMM_SOURCES = ("internal.h", "moe_gemm.hip", "moe_gemm_stream.hip", "moe_gemm_tiled.hip", "repack.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_grouped_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in GEMM_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -144,6 +149,87 @@ def route_align_timing(w, synthetic, dev, c, bm, reps: int = 50):
     return out
 
 
+def bench_grouped(args, layout: str):
+    """The layer on an expert-grouped layout over the 48-expert Kimi-K2 slice (H 7168, I 2048):
+    contiguous: the prefill_contig48 batch permuted into 48 x 128 rows (no padding);
+    masked: a 32-row budget per expert, all 32 rows live (the grouped decode case of
+    32 tokens per expert). One step = one entry-point call, cold caches."""
+    import torch
+
+    import synthetic
+    import w4a16_grouped_gemm_amd as w
+
+    c = synthetic.workload("prefill_contig48")
+    E, H, I = c.E, c.H, c.I
+    shape = w.make_shape(E, H, I)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).cuda()
+
+    n13, n2 = w.w4a16_packed_bytes(shape)
+    w13p = torch.empty(n13, dtype=torch.uint8, device="cuda")
+    w2p = torch.empty(n2, dtype=torch.uint8, device="cuda")
+    w.w4a16_repack(shape, dev(c.w13_q), dev(c.w13_s), dev(c.w2_q), dev(c.w2_s), w13p, w2p)
+    torch.cuda.synchronize()
+    if layout == "contiguous":
+        slots = np.argsort(c.topk_ids.reshape(-1), kind="stable")
+        m = c.topk_ids.reshape(-1)[slots].astype(np.int32)
+        x = dev(c.x[slots // c.topk])
+        M = len(m)
+        mi = dev(m)
+        ws = torch.empty(w.w4a16_moe_contiguous_workspace_bytes(shape, M), dtype=torch.uint8, device="cuda")
+        out = torch.empty((M, H), dtype=torch.int16, device="cuda")
+        bm, rows, name = 128, M, f"grouped_contiguous{E} ({E} experts x {M // E} rows, H {H}, I {I})"
+
+        def step():
+            w.w4a16_moe_contiguous_forward(shape, x, mi, w13p, w2p, out, ws)
+    else:
+        max_m = 32
+        x = dev(synthetic.make_x(E * max_m, H, seed=41).reshape(E, max_m, H))
+        mm = dev(np.full(E, max_m, np.int32))
+        bm = w.w4a16_moe_masked_block_m(max_m, max_m)
+        ws = torch.empty(w.w4a16_moe_masked_workspace_bytes(shape, max_m, bm), dtype=torch.uint8, device="cuda")
+        out = torch.empty((E, max_m, H), dtype=torch.int16, device="cuda")
+        rows, name = E * max_m, f"grouped_masked{E} ({E} experts x {max_m} live rows, H {H}, I {I})"
+
+        def step():
+            w.w4a16_moe_masked_forward(shape, x, mm, bm, w13p, w2p, out, ws)
+
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    for _ in range(args.warmup):
+        flush_buf.sum()
+        step()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        flush_buf.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    med = float(np.median(us))
+    w13 = H * 2 * I // 2 + (H // 32) * 2 * I * 2
+    w2 = I * H // 2 + (I // 32) * H * 2
+    layer_bytes = E * (w13 + w2) + rows * H * 2 * 2
+    layer_flops = 2 * rows * (H * 2 * I + I * H)
+    gbps, tflops = layer_bytes / (med * 1e-6) / 1e9, layer_flops / (med * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": f"W4A16 MoE layer µs, {layout} grouped layout", "value": round(med, 2), "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(med / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "rows": rows, "block_m": bm, "cache": "cold (1 GiB read before each step)"},
+        "layer_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "layer_TFLOPs": round(tflops, 2),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "alg_bytes": layer_bytes, "alg_flops": layer_flops,
+        "layer_us_p10_p90": [round(float(np.percentile(us, 10)), 2), round(float(np.percentile(us, 90)), 2)],
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +239,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0, help="0: the tokens-per-expert heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router", action="store_true", help="skip the router + alignment timing")
+    ap.add_argument("--layout", default="routed", choices=["routed", "contiguous", "masked"],
+                    help="routed: the layer on top-k routed ids (the default line); contiguous / masked: "
+                         "the grouped-layout entry points")
     ap.add_argument("--cpu-slots", type=int, default=64, help="resident slots the CPU baseline computes")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--copy-probe", action="store_true",
@@ -171,6 +260,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w.load()  # fail loudly if the HIP library is not built
+    if args.layout != "routed":
+        return bench_grouped(args, args.layout)
     print(f"[bench] building {args.workload}", file=sys.stderr, flush=True)
     c = synthetic.workload(args.workload)
     E, H, I, T, topk = c.E, c.H, c.I, c.T, c.topk

@@ -257,6 +257,58 @@ int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const 
 int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const int32_t* topk_ids,
                       const float* topk_weights, const float* y, uint16_t* out, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Expert-grouped activation layouts                                         */
+/* ------------------------------------------------------------------------ */
+
+/* The layer on the contiguous grouped layout of Chord's grouped kernels (Chord
+ * page, sections "핵심 기여" and "그룹 SM90 커널 기법": contiguous prefill, every
+ * expert's rows padded to a 128-row boundary). No routed ids and no alignment
+ * pass: the rows are already grouped.
+ *
+ *   x          device bf16 [M, H]; M a multiple of 128 (else W4A16_ERR_INVALID_ARG)
+ *   m_indices  device int32 [M]: the expert of each row; a value outside
+ *              [0, num_experts) marks a padding row. An expert's rows start at a
+ *              multiple of 128 and its padding rows follow its live rows, so a
+ *              128-row block holds one expert; a live row whose expert differs
+ *              from that of its block's first row is treated as padding.
+ *   out        device bf16 [M, H], every row written: out[r] = the row's down
+ *              output (fp32 accumulation, rounded once to bf16, no routing
+ *              weight), zeros for padding rows
+ *   workspace  device, >= w4a16_moe_contiguous_workspace_bytes(shape, M)
+ * Runs the index stage then w4a16_moe_forward's stages with block_m 128 and
+ * one slot of weight 1 per row. Same error codes as w4a16_moe_forward. */
+size_t w4a16_moe_contiguous_workspace_bytes(const w4a16_moe_shape* shape, int32_t M);
+int w4a16_moe_contiguous_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t M,
+                                 const int32_t* m_indices, const void* w13_packed, const void* w2_packed,
+                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* block_m for the masked layout: the tokens-per-expert rule of
+ * w4a16_choose_block_m applied to expected_m (the rows an expert is expected
+ * to hold; Chord page, "그룹 SM90 커널 기법": the block size follows the
+ * expected token count), halved until it divides max_m. 0 when max_m is not a
+ * positive multiple of 16 or expected_m < 0. */
+int32_t w4a16_moe_masked_block_m(int32_t max_m, int32_t expected_m);
+
+/* The layer on the masked grouped layout (Chord page, "그룹 SM90 커널 기법":
+ * masked decode reserves a fixed row budget per expert): a graph-friendly
+ * decode form whose buffers have a fixed size whatever the routing.
+ *
+ *   x          device bf16 [E, max_m, H]
+ *   max_m      rows per expert, a multiple of block_m (else W4A16_ERR_INVALID_ARG)
+ *   masked_m   device int32 [E]: live rows of each expert (rows 0 .. masked_m[e]-1;
+ *              values are clamped to [0, max_m])
+ *   block_m    16, 32, 64 or 128 (see w4a16_moe_masked_block_m)
+ *   out        device bf16 [E, max_m, H], every row written: the row's down
+ *              output for live rows, zeros for the others
+ *   workspace  device, >= w4a16_moe_masked_workspace_bytes(shape, max_m, block_m)
+ * Blocks of block_m rows past an expert's live rows are skipped by the GEMMs.
+ * Same error codes as w4a16_moe_forward. */
+size_t w4a16_moe_masked_workspace_bytes(const w4a16_moe_shape* shape, int32_t max_m, int32_t block_m);
+int w4a16_moe_masked_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t max_m,
+                             const int32_t* masked_m, int32_t block_m, const void* w13_packed, const void* w2_packed,
+                             uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -147,3 +147,34 @@ def moe_layer(x_bits, topk_ids, topk_weights, w13_q, w13_s, w2_q, w2_s, E: int, 
         _load().oracle_moe_layer(_ptr(x), T, H, I, E, topk, _ptr(ids), _ptr(wts), _ptr(q13), _ptr(s13),
                                  _ptr(q2), _ptr(s2), _ptr(tok), len(tok), 1 if round_h else 0, _ptr(out))
     return out
+
+
+def grouped_contiguous(x_bits, m_indices, w13_q, w13_s, w2_q, w2_s, E: int, I: int, rows=None,
+                       round_h: bool = True) -> np.ndarray:
+    """Contiguous grouped layout (Chord page, section "그룹 SM90 커널 기법": contiguous
+    prefill, each expert's rows padded to a 128-row boundary): row r belongs to expert
+    m_indices[r]; a value outside [0, E) marks padding. Output row r (fp64) is the
+    layer's per-slot result for that row alone, with no routing weight:
+    down_e(bf16(silu(gate_e x_r) * up_e x_r)); padding rows are zero. That is the
+    layer definition with one slot of weight 1 per row."""
+    ids = np.asarray(m_indices, np.int32).reshape(-1, 1)
+    ones = np.ones(ids.shape, np.float32)
+    return moe_layer(x_bits, ids, ones, w13_q, w13_s, w2_q, w2_s, E, I, tokens=rows, round_h=round_h)
+
+
+def masked_row_ids(masked_m, max_m: int) -> np.ndarray:
+    """Masked grouped layout (same page and section: a fixed budget of max_m rows per
+    expert): the expert of each of the E * max_m rows, -1 past masked_m[e]
+    (masked_m clamped to [0, max_m])."""
+    m = np.clip(np.asarray(masked_m, np.int64), 0, max_m)
+    E = len(m)
+    i = np.arange(max_m)[None, :]
+    return np.where(i < m[:, None], np.arange(E)[:, None], -1).astype(np.int32).reshape(-1)
+
+
+def grouped_masked(x_bits, masked_m, w13_q, w13_s, w2_q, w2_s, I: int, rows=None) -> np.ndarray:
+    """x_bits uint16 [E, max_m, H]; output [E * max_m, H] (fp64), or the listed flat rows."""
+    x = np.asarray(x_bits)
+    E, max_m, H = x.shape
+    return grouped_contiguous(x.reshape(E * max_m, H), masked_row_ids(masked_m, max_m), w13_q, w13_s, w2_q, w2_s,
+                              E, I, rows=rows)

@@ -68,10 +68,19 @@ class DeviceCase:
         return out.cpu().numpy().view(np.uint16)
 
 
-def parity(gpu_bits: np.ndarray, ref: np.ndarray, what: str):
-    """Assert the per-element bound; return the max of |err| / tol."""
+def parity(gpu_bits: np.ndarray, ref: np.ndarray, what: str, row_floor: bool = False):
+    """Assert the per-element bound; return the max of |err| / tol.
+
+    row_floor: for rows that are one unweighted slot (the grouped layouts), the floor of
+    the bound is also the row's largest |ref| / 32: a bf16 rounding of h that falls the
+    other way on the two sides (fp32 against fp64 sums of g and u) shifts every output
+    of the row by ulp(h_i) * |w2[c, i]|, an error that scales with the row, not with the
+    element. In the routed layer the routing weights (< 1, over top-k slots) scale the
+    same shift down, and the floor of 1 suffices."""
     g = bf16_to_f64(gpu_bits)
     tol = TOL * np.maximum(1.0, np.abs(ref))
+    if row_floor and ref.size:
+        tol = np.maximum(tol, TOL * np.abs(ref).max(axis=-1, keepdims=True) / 32)
     err = np.abs(g - ref)
     ratio = float((err / tol).max()) if err.size else 0.0
     nfail = int((err > tol).sum())

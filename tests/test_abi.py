@@ -117,6 +117,29 @@ def test_validation_status_codes(lib):
     cap = w.moe_align_capacity(16384, 8, 48, 128)
     assert ra(T=16384, Eg=384, topk=8, E=48, bm=128, cap=cap) == 4
     assert ra(T=16384, Eg=384, topk=8, E=48, bm=128, cap=cap, ws=FAKE, wsb=16) == 4
+    # grouped layouts
+    assert lib.w4a16_moe_contiguous_forward(ctypes.byref(good), FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                            None) == 1      # M not a multiple of 128
+    assert lib.w4a16_moe_contiguous_forward(ctypes.byref(good), FAKE, 128, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                            None) == 1      # null m_indices
+    need = w.w4a16_moe_contiguous_workspace_bytes(good, 256)
+    assert need > 0 and w.w4a16_moe_contiguous_workspace_bytes(good, 100) == 0
+    assert lib.w4a16_moe_contiguous_forward(ctypes.byref(good), FAKE, 256, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                            None) == 4
+    assert lib.w4a16_moe_masked_forward(ctypes.byref(good), FAKE, 40, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                        None) == 1          # max_m not a multiple of block_m
+    assert lib.w4a16_moe_masked_forward(ctypes.byref(good), FAKE, 48, FAKE, 24, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                        None) == 2          # unsupported block_m
+    need = w.w4a16_moe_masked_workspace_bytes(good, 32, 32)
+    assert need > 0 and w.w4a16_moe_masked_workspace_bytes(good, 40, 16) == 0
+    assert lib.w4a16_moe_masked_forward(ctypes.byref(good), FAKE, 32, FAKE, 32, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                        None) == 4
+    # masked block_m: the tokens-per-expert rule on expected_m, halved until it divides max_m
+    assert w.w4a16_moe_masked_block_m(32, 32) == 32
+    assert w.w4a16_moe_masked_block_m(256, 32) == 64
+    assert w.w4a16_moe_masked_block_m(256, 200) == 128
+    assert w.w4a16_moe_masked_block_m(48, 4) == 16
+    assert w.w4a16_moe_masked_block_m(40, 4) == 0          # not a multiple of 16
     # repack and stages
     assert lib.w4a16_repack(ctypes.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1

@@ -14,7 +14,9 @@ from ._lib import LIB_PATH, Shape, load
 __all__ = [
     "W4A16Error", "Shape", "LIB_PATH", "load", "make_shape", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "moe_align_capacity", "moe_align_workspace_bytes", "w4a16_choose_block_m", "moe_align",
-    "moe_route_align", "w4a16_moe_stage_workspace_bytes", "w4a16_moe_prepare_x", "w4a16_moe_prepare_h",
+    "moe_route_align", "w4a16_moe_contiguous_workspace_bytes", "w4a16_moe_contiguous_forward",
+    "w4a16_moe_masked_block_m", "w4a16_moe_masked_workspace_bytes", "w4a16_moe_masked_forward",
+    "w4a16_moe_stage_workspace_bytes", "w4a16_moe_prepare_x", "w4a16_moe_prepare_h",
     "w4a16_moe_workspace_bytes", "w4a16_moe_forward", "w4a16_moe_gate_up", "w4a16_moe_down",
     "w4a16_moe_combine", "align_buffers",
 ]
@@ -93,6 +95,33 @@ def moe_route_align(logits, topk: int, num_experts: int, block_m: int, topk_ids,
                                   _p(topk_weights), _p(sorted_token_ids), sorted_token_ids.numel(), _p(expert_ids),
                                   _p(num_tokens_post_padded), _p(expert_counts), _p(workspace), _nbytes(workspace),
                                   _stream(stream)), "moe_route_align")
+
+
+def w4a16_moe_contiguous_workspace_bytes(shape: Shape, M: int) -> int:
+    return load().w4a16_moe_contiguous_workspace_bytes(ctypes.byref(shape), M)
+
+
+def w4a16_moe_contiguous_forward(shape: Shape, x, m_indices, w13_packed, w2_packed, out, workspace, stream=None):
+    M = x.shape[0]
+    _check(load().w4a16_moe_contiguous_forward(ctypes.byref(shape), _p(x), M, _p(m_indices), _p(w13_packed),
+                                               _p(w2_packed), _p(out), _p(workspace), _nbytes(workspace),
+                                               _stream(stream)), "w4a16_moe_contiguous_forward")
+
+
+def w4a16_moe_masked_block_m(max_m: int, expected_m: int) -> int:
+    return load().w4a16_moe_masked_block_m(max_m, expected_m)
+
+
+def w4a16_moe_masked_workspace_bytes(shape: Shape, max_m: int, block_m: int) -> int:
+    return load().w4a16_moe_masked_workspace_bytes(ctypes.byref(shape), max_m, block_m)
+
+
+def w4a16_moe_masked_forward(shape: Shape, x, masked_m, block_m: int, w13_packed, w2_packed, out, workspace,
+                             stream=None):
+    max_m = x.shape[1]
+    _check(load().w4a16_moe_masked_forward(ctypes.byref(shape), _p(x), max_m, _p(masked_m), block_m,
+                                           _p(w13_packed), _p(w2_packed), _p(out), _p(workspace),
+                                           _nbytes(workspace), _stream(stream)), "w4a16_moe_masked_forward")
 
 
 def w4a16_moe_workspace_bytes(shape: Shape, T: int, topk: int, block_m: int) -> int:

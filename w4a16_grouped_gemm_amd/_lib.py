@@ -27,6 +27,11 @@ SIGNATURES = {
     "w4a16_choose_block_m": (I32, [I32, I32, I32, I32]),
     "moe_align": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, P, P, P, SZ, P]),
     "moe_route_align": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P]),
+    "w4a16_moe_contiguous_workspace_bytes": (SZ, [P, I32]),
+    "w4a16_moe_contiguous_forward": (ctypes.c_int, [P, P, I32, P, P, P, P, P, SZ, P]),
+    "w4a16_moe_masked_block_m": (I32, [I32, I32]),
+    "w4a16_moe_masked_workspace_bytes": (SZ, [P, I32, I32]),
+    "w4a16_moe_masked_forward": (ctypes.c_int, [P, P, I32, P, I32, P, P, P, P, SZ, P]),
     "w4a16_moe_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_stage_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_forward": (ctypes.c_int, [P, P, I32, I32, P, P, P, I32, P, P, I32, P, P, P, P, SZ, P]),

@@ -325,3 +325,103 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
 }
 
 }  // extern "C"
+
+namespace {
+// Workspace of the grouped-layout entry points: row_ids [M] | ones [M] |
+// sorted [capacity] | expert_ids [nblk] | ntpp | the layer's own workspace.
+struct GroupedWorkspace {
+  size_t row_ids, ones, sorted, expert_ids, ntpp, layer, layer_bytes, total;
+  int32_t capacity;
+};
+
+GroupedWorkspace grouped_workspace(const w4a16_moe_shape* s, int32_t M, int32_t bm) {
+  GroupedWorkspace g{};
+  g.capacity = (int32_t)moe_align_capacity(M, 1, s->num_experts, bm);
+  const size_t nblk = ((size_t)g.capacity + bm - 1) / bm;
+  g.row_ids = 0;
+  g.ones = g.row_ids + round_up((size_t)M * 4);
+  g.sorted = g.ones + round_up((size_t)M * 4);
+  g.expert_ids = g.sorted + round_up((size_t)g.capacity * 4);
+  g.ntpp = g.expert_ids + round_up(nblk * 4);
+  g.layer = g.ntpp + kAlign;
+  g.layer_bytes = w4a16_moe_workspace_bytes(s, M, 1, bm);
+  g.total = g.layer + g.layer_bytes;
+  return g;
+}
+
+constexpr int32_t kContiguousBlockM = 128;
+
+int grouped_forward(GroupedLayout kind, const w4a16_moe_shape* shape, const uint16_t* x, int32_t M, int32_t max_m,
+                    const int32_t* m_indices, const int32_t* masked_m, int32_t block_m, const void* w13_packed,
+                    const void* w2_packed, uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const GroupedWorkspace g = grouped_workspace(shape, M, block_m);
+  if (!workspace || workspace_bytes < g.total) return W4A16_ERR_WORKSPACE;
+  if (M == 0) return W4A16_OK;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* row_ids = reinterpret_cast<int32_t*>(ws + g.row_ids);
+  float* ones = reinterpret_cast<float*>(ws + g.ones);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + g.sorted);
+  int32_t* expert_ids = reinterpret_cast<int32_t*>(ws + g.expert_ids);
+  int32_t* ntpp = reinterpret_cast<int32_t*>(ws + g.ntpp);
+  const hipError_t e = launch_grouped_index(kind, m_indices, masked_m, M, max_m, shape->num_experts, block_m, row_ids,
+                                            ones, sorted, g.capacity, expert_ids, ntpp,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return W4A16_ERR_HIP;
+  // every row is one slot (topk 1) with weight 1: the layer's output row is the row's down output
+  return w4a16_moe_forward(shape, x, M, 1, row_ids, ones, sorted, g.capacity, expert_ids, ntpp, block_m, w13_packed,
+                           w2_packed, out, ws + g.layer, g.layer_bytes, stream);
+}
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_moe_contiguous_workspace_bytes(const w4a16_moe_shape* shape, int32_t M) {
+  if (check_shape(shape) != W4A16_OK || M < 0 || M % kContiguousBlockM != 0) return 0;
+  if (check_tokens(M, 1, shape->num_experts, kContiguousBlockM) != W4A16_OK) return 0;
+  return grouped_workspace(shape, M, kContiguousBlockM).total;
+}
+
+int w4a16_moe_contiguous_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t M,
+                                 const int32_t* m_indices, const void* w13_packed, const void* w2_packed,
+                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  if (M < 0 || M % kContiguousBlockM != 0) return W4A16_ERR_INVALID_ARG;
+  st = check_tokens(M, 1, shape->num_experts, kContiguousBlockM);
+  if (st != W4A16_OK) return st;
+  if ((M > 0 && (!x || !m_indices || !out)) || !w13_packed || !w2_packed) return W4A16_ERR_INVALID_ARG;
+  return grouped_forward(kContiguous, shape, x, M, 0, m_indices, nullptr, kContiguousBlockM, w13_packed, w2_packed,
+                         out, workspace, workspace_bytes, stream);
+}
+
+int32_t w4a16_moe_masked_block_m(int32_t max_m, int32_t expected_m) {
+  if (max_m < 16 || max_m % 16 != 0 || expected_m < 0) return 0;
+  int32_t bm = w4a16_choose_block_m(expected_m, 1, 1, 1);  // tokens per expert = expected_m
+  while (max_m % bm != 0) bm /= 2;
+  return bm;
+}
+
+size_t w4a16_moe_masked_workspace_bytes(const w4a16_moe_shape* shape, int32_t max_m, int32_t block_m) {
+  if (check_shape(shape) != W4A16_OK || !block_m_ok(block_m) || max_m < 0 || max_m % block_m != 0) return 0;
+  const int64_t M = (int64_t)shape->num_experts * max_m;
+  if (M > INT_MAX || check_tokens((int32_t)M, 1, shape->num_experts, block_m) != W4A16_OK) return 0;
+  return grouped_workspace(shape, (int32_t)M, block_m).total;
+}
+
+int w4a16_moe_masked_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t max_m,
+                             const int32_t* masked_m, int32_t block_m, const void* w13_packed, const void* w2_packed,
+                             uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  if (!block_m_ok(block_m)) return W4A16_ERR_UNSUPPORTED;
+  if (max_m < 0 || max_m % block_m != 0) return W4A16_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)shape->num_experts * max_m;
+  if (M > INT_MAX) return W4A16_ERR_UNSUPPORTED;
+  st = check_tokens((int32_t)M, 1, shape->num_experts, block_m);
+  if (st != W4A16_OK) return st;
+  if ((M > 0 && (!x || !masked_m || !out)) || !w13_packed || !w2_packed) return W4A16_ERR_INVALID_ARG;
+  return grouped_forward(kMasked, shape, x, (int32_t)M, max_m, nullptr, masked_m, block_m, w13_packed, w2_packed,
+                         out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -96,6 +96,19 @@ hipError_t launch_route_align(const float* logits, const float* bias, int32_t T,
                               int32_t capacity, int32_t* expert_ids, int32_t* ntpp, int32_t* counts, void* workspace,
                               hipStream_t stream);
 
+// Alignment buffers for the expert-grouped activation layouts (no routed ids):
+// kContiguous takes a per-row expert index m_indices [M]; kMasked takes
+// masked_m [E] live rows of each expert's max_m-row budget (M = E * max_m).
+// Writes sorted [capacity] (p for a live row p, else the sentinel M),
+// expert_ids [ceil(capacity / block_m)] (the expert of the block's first row,
+// -1 when that row is not live), *ntpp = M, ones [M] = 1.0f and row_ids [M]
+// (the row's expert, or -1 for a row that is not live).
+enum GroupedLayout { kContiguous = 0, kMasked = 1 };
+hipError_t launch_grouped_index(GroupedLayout kind, const int32_t* m_indices, const int32_t* masked_m, int32_t M,
+                                int32_t max_m, int32_t E, int32_t block_m, int32_t* row_ids, float* ones,
+                                int32_t* sorted, int32_t capacity, int32_t* expert_ids, int32_t* ntpp,
+                                hipStream_t stream);
+
 // Writes all four regions of one projection's packed buffer.
 hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int32_t E, int32_t N, int32_t K,
                          int32_t interleave_I, uint8_t* packed, hipStream_t stream);
