@@ -5,10 +5,13 @@
  * symmetric INT4 with one BF16 scale per group of 32 along the reduction
  * dimension ("W4A16 그룹 스케일 형식", group-32 key: Chord page "vLLM 및 Novita AI,
  * Kimi K2.x용 더 빠른 INT4 MoE 커널 출시: Chord", sections "vLLM과의 통합" and
- * "런타임 고려사항"). Three stages run on the caller's HIP stream:
+ * "런타임 고려사항"). The entry points, all on the caller's HIP stream:
  *
  *   moe_align           topk_ids -> sorted_token_ids, expert_ids, num_tokens_post_padded
+ *   moe_route_align     router logits -> top-k ids and weights, then moe_align
  *   w4a16_moe_forward   gate_up GEMM + SiLU-and-mul, down GEMM, top-k weighted combine
+ *   w4a16_moe_contiguous_forward / w4a16_moe_masked_forward
+ *                       the layer on expert-grouped activation layouts
  *   w4a16_repack        once at weight load: canonical int4 + scales -> kernel layout
  *
  * Conventions shared by every entry point
@@ -30,6 +33,9 @@
  * Routing ids outside [0, num_experts) mean "expert not resident in this call"
  *   (one GPU's expert slice) and are skipped, not errors; weights are used as given.
  * Dtypes: bf16 values travel as their uint16_t bit patterns.
+ * Alignment: activation, weight, output and workspace buffers are moved 16
+ *   bytes at a time and must be 16-byte aligned (W4A16_ERR_INVALID_ARG
+ *   otherwise); torch and hipMalloc allocations are.
  */
 #ifndef W4A16_MOE_H
 #define W4A16_MOE_H
@@ -276,8 +282,9 @@ int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, con
  *              output (fp32 accumulation, rounded once to bf16, no routing
  *              weight), zeros for padding rows
  *   workspace  device, >= w4a16_moe_contiguous_workspace_bytes(shape, M)
- * Runs the index stage then w4a16_moe_forward's stages with block_m 128 and
- * one slot of weight 1 per row. Same error codes as w4a16_moe_forward. */
+ * Runs an index stage (which also zeroes the padding rows of out), then the
+ * layer's stages with block_m 128 and one slot per row; the down GEMM writes
+ * the live rows of out directly. Same error codes as w4a16_moe_forward. */
 size_t w4a16_moe_contiguous_workspace_bytes(const w4a16_moe_shape* shape, int32_t M);
 int w4a16_moe_contiguous_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t M,
                                  const int32_t* m_indices, const void* w13_packed, const void* w2_packed,
@@ -302,8 +309,9 @@ int32_t w4a16_moe_masked_block_m(int32_t max_m, int32_t expected_m);
  *   out        device bf16 [E, max_m, H], every row written: the row's down
  *              output for live rows, zeros for the others
  *   workspace  device, >= w4a16_moe_masked_workspace_bytes(shape, max_m, block_m)
- * Blocks of block_m rows past an expert's live rows are skipped by the GEMMs.
- * Same error codes as w4a16_moe_forward. */
+ * Blocks of block_m rows past an expert's live rows are skipped by the GEMMs;
+ * the down GEMM writes the live rows of out directly. Same error codes as
+ * w4a16_moe_forward. */
 size_t w4a16_moe_masked_workspace_bytes(const w4a16_moe_shape* shape, int32_t max_m, int32_t block_m);
 int w4a16_moe_masked_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t max_m,
                              const int32_t* masked_m, int32_t block_m, const void* w13_packed, const void* w2_packed,

@@ -96,6 +96,10 @@ def test_validation_status_codes(lib):
     assert _fwd(lib, good, cap=w.moe_align_capacity(4, 2, 8, 16) - 1) == 3
     assert _fwd(lib, good, ws_bytes=100) == 4
     assert _fwd(lib, good, ws=None) == 4
+    odd_ptr = ctypes.c_void_p(0x1008)                        # 8-byte aligned only
+    assert _fwd(lib, good, x=odd_ptr) == 1
+    assert _fwd(lib, good, ws=odd_ptr) == 1
+    assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 2, FAKE, FAKE, FAKE, odd_ptr, None) == 1
     # alignment
     assert lib.moe_align(FAKE, 4, 2, 8, 16, FAKE, 10, FAKE, FAKE, None, None, 0, None) == 3
     assert lib.moe_align(FAKE, 4, 2, 8, 24, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 2

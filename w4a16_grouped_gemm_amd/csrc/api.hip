@@ -42,6 +42,13 @@ int check_tokens(int32_t T, int32_t topk, int32_t E, int32_t block_m) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+// The kernels move activations, weights and outputs 16 bytes at a time.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+template <typename... Ps>
+bool all_aligned16(const Ps*... ps) {
+  return (aligned16(ps) && ...);
+}
+
 GemmParams gemm_params(const w4a16_moe_shape* s, int32_t T, int32_t topk, const int32_t* sorted, int32_t capacity,
                        const int32_t* expert_ids, const int32_t* ntpp, const void* packed, int32_t N, int32_t K) {
   GemmParams p{};
@@ -195,6 +202,7 @@ int w4a16_moe_prepare_x(const w4a16_moe_shape* shape, const uint16_t* x, int32_t
   st = check_tokens(T, topk, shape->num_experts, block_m);
   if (st != W4A16_OK) return st;
   if (T > 0 && (!x || !topk_ids)) return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(x, workspace)) return W4A16_ERR_INVALID_ARG;
   st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
   if (!tiled_gemm_supported(block_m, 2 * shape->intermediate, shape->hidden)) return W4A16_OK;  // nothing to prepare
@@ -212,6 +220,7 @@ int w4a16_moe_gate_up(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
   if (st != W4A16_OK) return st;
   if ((T > 0 && !x) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w13_packed || !h)
     return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(x, w13_packed, h, workspace)) return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
   st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
@@ -233,6 +242,7 @@ int w4a16_moe_prepare_h(const w4a16_moe_shape* shape, int32_t T, int32_t topk, c
   st = check_tokens(T, topk, shape->num_experts, block_m);
   if (st != W4A16_OK) return st;
   if (!h || !sorted_token_ids || !num_tokens_post_padded) return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(h, workspace)) return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
   st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
@@ -255,6 +265,7 @@ int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const 
   if (st != W4A16_OK) return st;
   if (!h || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !w2_packed || (T > 0 && !y))
     return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(h, w2_packed, y, workspace)) return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
   st = check_stage_workspace(shape, T, topk, block_m, workspace, workspace_bytes);
@@ -279,6 +290,7 @@ int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, con
   if (topk > W4A16_MAX_TOPK) return W4A16_ERR_UNSUPPORTED;
   if ((int64_t)T * topk > INT_MAX / 2) return W4A16_ERR_UNSUPPORTED;
   if (T > 0 && (!topk_ids || !topk_weights || !y || !out)) return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(y, out)) return W4A16_ERR_INVALID_ARG;
   return hip_status(launch_combine(topk_ids, topk_weights, y, out, T, topk, shape->hidden, shape->num_experts,
                                    static_cast<hipStream_t>(stream)));
 }
@@ -295,6 +307,7 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
   if ((T > 0 && (!x || !topk_ids || !topk_weights || !out)) || !sorted_token_ids || !expert_ids ||
       !num_tokens_post_padded || !w13_packed || !w2_packed)
     return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(x, out, w13_packed, w2_packed, workspace)) return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, shape->num_experts, block_m))
     return W4A16_ERR_CAPACITY;
   const size_t need = w4a16_moe_workspace_bytes(shape, T, topk, block_m);
@@ -327,10 +340,12 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
 }  // extern "C"
 
 namespace {
-// Workspace of the grouped-layout entry points: row_ids [M] | ones [M] |
-// sorted [capacity] | expert_ids [nblk] | ntpp | the layer's own workspace.
+// Workspace of the grouped-layout entry points: row_ids [M] |
+// sorted [capacity] | expert_ids [nblk] | ntpp | h [capacity, I] bf16 | the
+// GEMM stages' scratch. The down GEMM writes the output rows directly (bf16),
+// so there is no fp32 row buffer and no combine pass.
 struct GroupedWorkspace {
-  size_t row_ids, ones, sorted, expert_ids, ntpp, layer, layer_bytes, total;
+  size_t row_ids, sorted, expert_ids, ntpp, h, scratch, scratch_bytes, total;
   int32_t capacity;
 };
 
@@ -339,13 +354,13 @@ GroupedWorkspace grouped_workspace(const w4a16_moe_shape* s, int32_t M, int32_t 
   g.capacity = (int32_t)moe_align_capacity(M, 1, s->num_experts, bm);
   const size_t nblk = ((size_t)g.capacity + bm - 1) / bm;
   g.row_ids = 0;
-  g.ones = g.row_ids + round_up((size_t)M * 4);
-  g.sorted = g.ones + round_up((size_t)M * 4);
+  g.sorted = g.row_ids + round_up((size_t)M * 4);
   g.expert_ids = g.sorted + round_up((size_t)g.capacity * 4);
   g.ntpp = g.expert_ids + round_up(nblk * 4);
-  g.layer = g.ntpp + kAlign;
-  g.layer_bytes = w4a16_moe_workspace_bytes(s, M, 1, bm);
-  g.total = g.layer + g.layer_bytes;
+  g.h = g.ntpp + kAlign;
+  g.scratch = g.h + round_up((size_t)g.capacity * s->intermediate * 2);
+  g.scratch_bytes = w4a16_moe_stage_workspace_bytes(s, M, 1, bm);
+  g.total = g.scratch + g.scratch_bytes;
   return g;
 }
 
@@ -354,22 +369,38 @@ constexpr int32_t kContiguousBlockM = 128;
 int grouped_forward(GroupedLayout kind, const w4a16_moe_shape* shape, const uint16_t* x, int32_t M, int32_t max_m,
                     const int32_t* m_indices, const int32_t* masked_m, int32_t block_m, const void* w13_packed,
                     const void* w2_packed, uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!all_aligned16(x, out, w13_packed, w2_packed, workspace)) return W4A16_ERR_INVALID_ARG;
   const GroupedWorkspace g = grouped_workspace(shape, M, block_m);
   if (!workspace || workspace_bytes < g.total) return W4A16_ERR_WORKSPACE;
   if (M == 0) return W4A16_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* row_ids = reinterpret_cast<int32_t*>(ws + g.row_ids);
-  float* ones = reinterpret_cast<float*>(ws + g.ones);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + g.sorted);
   int32_t* expert_ids = reinterpret_cast<int32_t*>(ws + g.expert_ids);
   int32_t* ntpp = reinterpret_cast<int32_t*>(ws + g.ntpp);
-  const hipError_t e = launch_grouped_index(kind, m_indices, masked_m, M, max_m, shape->num_experts, block_m, row_ids,
-                                            ones, sorted, g.capacity, expert_ids, ntpp,
-                                            static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return W4A16_ERR_HIP;
-  // every row is one slot (topk 1) with weight 1: the layer's output row is the row's down output
-  return w4a16_moe_forward(shape, x, M, 1, row_ids, ones, sorted, g.capacity, expert_ids, ntpp, block_m, w13_packed,
-                           w2_packed, out, ws + g.layer, g.layer_bytes, stream);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + g.h);
+  void* scratch = ws + g.scratch;
+  const int32_t H = shape->hidden, I = shape->intermediate;
+  // index buffers, and zeros in the output rows that are not live
+  int rc = hip_status(launch_grouped_index(kind, m_indices, masked_m, M, max_m, shape->num_experts, block_m, row_ids,
+                                           sorted, g.capacity, expert_ids, ntpp, out, H, st));
+  if (rc != W4A16_OK) return rc;
+  // every row is one slot (topk 1): the layer's stages up to down
+  rc = w4a16_moe_prepare_x(shape, x, M, 1, row_ids, block_m, scratch, g.scratch_bytes, stream);
+  if (rc != W4A16_OK) return rc;
+  rc = w4a16_moe_gate_up(shape, x, M, 1, sorted, g.capacity, expert_ids, ntpp, block_m, w13_packed, h, scratch,
+                         g.scratch_bytes, stream);
+  if (rc != W4A16_OK) return rc;
+  rc = w4a16_moe_prepare_h(shape, M, 1, h, sorted, g.capacity, ntpp, block_m, scratch, g.scratch_bytes, stream);
+  if (rc != W4A16_OK) return rc;
+  // down writes each live row's result straight into out, rounded once to bf16
+  GemmParams p = gemm_params(shape, M, 1, sorted, g.capacity, expert_ids, ntpp, w2_packed, H, I);
+  p.a = h;
+  p.out = out;
+  p.out_ld = H;
+  p.out_bf16 = 1;
+  return hip_status(launch_moe_gemm(kDown, block_m, p, scratch, st));
 }
 }  // namespace
 

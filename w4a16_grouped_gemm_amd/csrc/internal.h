@@ -70,7 +70,7 @@ struct GemmParams {
   const int32_t* sorted;   // sorted_token_ids [capacity]
   const int32_t* expert_ids;
   const int32_t* ntpp;     // num_tokens_post_padded (device)
-  void* out;               // gate_up: h bf16 [capacity, I]; down: y fp32 [n_slots, H]
+  void* out;               // gate_up: h bf16 [capacity, I]; down: y fp32 [n_slots, H] (bf16 with out_bf16)
   int32_t K;               // reduction length (H or I)
   int32_t N;               // output channels (2I or H)
   int32_t E;
@@ -78,6 +78,7 @@ struct GemmParams {
   int32_t n_slots;         // T * topk: ids >= this are padding
   int32_t capacity;
   int32_t out_ld;          // leading dimension of out (I or H)
+  int32_t out_bf16;        // down only: write each slot's row rounded to bf16 instead of fp32
 };
 
 enum GemmMode { kGateUp = 0, kDown = 1 };
@@ -101,12 +102,14 @@ hipError_t launch_route_align(const float* logits, const float* bias, int32_t T,
 // masked_m [E] live rows of each expert's max_m-row budget (M = E * max_m).
 // Writes sorted [capacity] (p for a live row p, else the sentinel M),
 // expert_ids [ceil(capacity / block_m)] (the expert of the block's first row,
-// -1 when that row is not live), *ntpp = M, ones [M] = 1.0f and row_ids [M]
-// (the row's expert, or -1 for a row that is not live).
+// -1 when that row is not live), *ntpp = M and row_ids [M] (the row's expert,
+// or -1 for a row that is not live).
+// Then, when out is not null, zeroes the rows of out [M, H] (bf16) that are not
+// live (the GEMMs write only live rows).
 enum GroupedLayout { kContiguous = 0, kMasked = 1 };
 hipError_t launch_grouped_index(GroupedLayout kind, const int32_t* m_indices, const int32_t* masked_m, int32_t M,
-                                int32_t max_m, int32_t E, int32_t block_m, int32_t* row_ids, float* ones,
-                                int32_t* sorted, int32_t capacity, int32_t* expert_ids, int32_t* ntpp,
+                                int32_t max_m, int32_t E, int32_t block_m, int32_t* row_ids, int32_t* sorted,
+                                int32_t capacity, int32_t* expert_ids, int32_t* ntpp, uint16_t* out, int32_t H,
                                 hipStream_t stream);
 
 // Writes all four regions of one projection's packed buffer.

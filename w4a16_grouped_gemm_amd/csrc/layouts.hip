@@ -9,8 +9,9 @@
 // Neither needs an alignment pass over routed ids: this kernel writes the
 // alignment buffers the GEMM stages read (row position p maps to row p; one
 // expert per block_m-row block, -1 for blocks without a live first row) plus
-// a per-row expert id and unit weights for the final per-row conversion. One
-// thread per position, grid-strided; every output is written on every call.
+// a per-row expert id, and zeroes the output rows that are not live (the down
+// GEMM writes the live ones). One thread per position, grid-strided; every
+// output is written on every call.
 // block_m is a power of two and, for the masked layout, divides max_m.
 #include "internal.h"
 
@@ -22,7 +23,7 @@ namespace {
 __global__ __launch_bounds__(256) void grouped_index_kernel(GroupedLayout kind, const int32_t* __restrict__ m_indices,
                                                             const int32_t* __restrict__ masked_m, int32_t M,
                                                             int32_t max_m, int32_t E, int32_t bm,
-                                                            int32_t* __restrict__ row_ids, float* __restrict__ ones,
+                                                            int32_t* __restrict__ row_ids,
                                                             int32_t* __restrict__ sorted, int32_t capacity,
                                                             int32_t* __restrict__ expert_ids, int32_t nblk,
                                                             int32_t* __restrict__ ntpp) {
@@ -46,25 +47,38 @@ __global__ __launch_bounds__(256) void grouped_index_kernel(GroupedLayout kind, 
     int e = expert_of(p);
     if (e >= 0 && kind == kContiguous && expert_of(p & -bm) != e) e = -1;
     sorted[p] = e >= 0 ? p : M;  // sentinel M: not a live row
-    if (p < M) {
-      ones[p] = 1.0f;
-      row_ids[p] = e;
-    }
+    if (p < M) row_ids[p] = e;
   }
   for (int b = t0; b < nblk; b += step) expert_ids[b] = expert_of(b * bm);
   if (t0 == 0) *ntpp = M;
 }
 
+// Zeroes the rows of out [M, H] bf16 whose row_ids entry is negative, 16 bytes
+// per thread and step (H is a multiple of 8).
+__global__ __launch_bounds__(256) void zero_dead_rows_kernel(const int32_t* __restrict__ row_ids, int32_t M, int32_t H,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t chunks_per_row = H / 8;
+  const int64_t total = (int64_t)M * chunks_per_row;
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = c / chunks_per_row;
+    if (row_ids[row] < 0) reinterpret_cast<uint4*>(out)[c] = zero;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_grouped_index(GroupedLayout kind, const int32_t* m_indices, const int32_t* masked_m, int32_t M,
-                                int32_t max_m, int32_t E, int32_t block_m, int32_t* row_ids, float* ones,
-                                int32_t* sorted, int32_t capacity, int32_t* expert_ids, int32_t* ntpp,
-                                hipStream_t stream) {
+                                int32_t max_m, int32_t E, int32_t block_m, int32_t* row_ids, int32_t* sorted, int32_t capacity, int32_t* expert_ids, int32_t* ntpp,
+                                uint16_t* out, int32_t H, hipStream_t stream) {
   const int nblk = (capacity + block_m - 1) / block_m;
   const int grid = (int)std::min<int64_t>(2048, std::max<int64_t>(1, ((int64_t)capacity + 255) / 256));
   hipLaunchKernelGGL(grouped_index_kernel, dim3(grid), dim3(256), 0, stream, kind, m_indices, masked_m, M, max_m, E,
-                     block_m, row_ids, ones, sorted, capacity, expert_ids, nblk, ntpp);
+                     block_m, row_ids, sorted, capacity, expert_ids, nblk, ntpp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !out || M == 0) return err;
+  const int zgrid = (int)std::min<int64_t>(4096, ((int64_t)M * (H / 8) + 255) / 256);
+  hipLaunchKernelGGL(zero_dead_rows_kernel, dim3(zgrid), dim3(256), 0, stream, row_ids, M, H, out);
   return hipGetLastError();
 }
 

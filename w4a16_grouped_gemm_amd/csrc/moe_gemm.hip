@@ -230,6 +230,10 @@ __global__ __launch_bounds__(256) void moe_gemm_stream_kernel(GemmParams p) {
           __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + (lane & 15);
           h[0] = (__bf16)silu_mul(acc[rb][0][i], acc[rb][2][i]);
           h[16] = (__bf16)silu_mul(acc[rb][1][i], acc[rb][3][i]);
+        } else if (p.out_bf16) {
+          __bf16* o = static_cast<__bf16*>(p.out) + (int64_t)id * p.out_ld + nb * kNBlock + (lane & 15);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[16 * c] = (__bf16)acc[rb][c][i];
         } else {
           float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + nb * kNBlock + (lane & 15);
 #pragma unroll

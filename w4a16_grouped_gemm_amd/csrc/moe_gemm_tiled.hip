@@ -255,6 +255,10 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
       if (MODE == kGateUp) {
         __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + 16 * HALF + (lane & 15);
         h[0] = (__bf16)silu_mul(v0, v1);
+      } else if (p.out_bf16) {
+        __bf16* o = static_cast<__bf16*>(p.out) + (int64_t)id * p.out_ld + pc0;
+        o[0] = (__bf16)v0;
+        o[32] = (__bf16)v1;
       } else {
         float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + pc0;
         y[0] = v0;
