@@ -268,6 +268,9 @@ def main():
     Eg = c.meta.get("E_global", E)
     bm = args.block_m or w.w4a16_choose_block_m(T, topk, E, Eg)
     shape = w.make_shape(E, H, I)
+    # the product path is the one-call routed layer (alignment included); --block-m forces
+    # one alignment at that size through w4a16_moe_forward instead
+    split = 0 if args.block_m else w.w4a16_moe_routed_split(shape, T, topk, Eg)
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -283,13 +286,19 @@ def main():
     torch.cuda.synchronize()
     del q13, s13, q2, s2
     x, ids, wts = dev(c.x), dev(c.topk_ids.astype(np.int32)), dev(c.topk_weights.astype(np.float32))
-    buf = w.align_buffers(T, topk, E, bm)
-    cap = buf["sorted_token_ids"].numel()
-    ws = torch.empty(w.w4a16_moe_workspace_bytes(shape, T, topk, bm), dtype=torch.uint8, device="cuda")
-    h = ws[: ((cap * I * 2 + 255) // 256) * 256].view(torch.int16)[: cap * I].view(cap, I)
-    y_off = ((cap * I * 2 + 255) // 256) * 256
-    y = ws[y_off: y_off + T * topk * H * 4].view(torch.float32).view(T * topk, H)
-    scratch = ws[y_off + ((T * topk * H * 4 + 255) // 256) * 256:]
+    # staged replica of the path: one alignment set, or (split) the heavy set at block_m 128
+    # and the light set at 16, each with its own h rows
+    sets = [(128, split, 2**31 - 1), (16, 1, split - 1)] if split else [(bm, 0, 2**31 - 1)]
+    bufs = [w.align_buffers(T, topk, E, b) for b, _, _ in sets]
+    hs = [torch.empty((b["sorted_token_ids"].numel(), I), dtype=torch.int16, device="cuda") for b in bufs]
+    y = torch.empty((T * topk, H), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(max(256, w.w4a16_moe_stage_workspace_bytes(shape, T, topk, sets[0][0])), dtype=torch.uint8,
+                          device="cuda")
+    bm = sets[0][0]
+    if args.block_m:
+        ws = torch.empty(w.w4a16_moe_workspace_bytes(shape, T, topk, bm), dtype=torch.uint8, device="cuda")
+    else:
+        ws = torch.empty(w.w4a16_moe_routed_workspace_bytes(shape, T, topk, Eg), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     flush_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")  # 1 GiB, read to evict caches
 
@@ -297,32 +306,50 @@ def main():
         flush_buf.sum()
 
     def align():
-        w.moe_align(ids, E, bm, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"], None,
-                    buf["workspace"])
+        for (b, lo, hi), buf in zip(sets, bufs):
+            w.moe_align_filtered(ids, E, b, lo, hi, buf["sorted_token_ids"], buf["expert_ids"],
+                                 buf["num_tokens_post_padded"], None, buf["workspace"])
 
-    srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+    def gemm(stage, k):
+        b, buf = sets[k][0], bufs[k]
+        srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+        if stage == "gate_up":
+            w.w4a16_moe_gate_up(shape, x, T, topk, srt, eid, ntpp, b, w13p, hs[k], scratch)
+        else:
+            w.w4a16_moe_down(shape, T, topk, hs[k], srt, eid, ntpp, b, w2p, y, scratch)
+
+    # stage names, in order; one event between consecutive stages
+    names = ["align", "prepare_x", "gate_up"] + (["gate_up_light"] if split else []) + ["prepare_h", "down"] + \
+        (["down_light"] if split else []) + ["combine"]
 
     def stages(ev):
-        # one event between consecutive stages: align, prepare_x, gate_up, prepare_h, down, combine
-        ev[0].record()
+        marks = iter(ev)
+        next(marks).record()
         align()
-        ev[1].record()
+        next(marks).record()
         w.w4a16_moe_prepare_x(shape, x, ids, bm, scratch)
-        ev[2].record()
-        w.w4a16_moe_gate_up(shape, x, T, topk, srt, eid, ntpp, bm, w13p, h, scratch)
-        ev[3].record()
-        w.w4a16_moe_prepare_h(shape, T, topk, h, srt, ntpp, bm, scratch)
-        ev[4].record()
-        w.w4a16_moe_down(shape, T, topk, h, srt, eid, ntpp, bm, w2p, y, scratch)
-        ev[5].record()
+        for k in range(len(sets)):
+            next(marks).record()
+            gemm("gate_up", k)
+        next(marks).record()
+        w.w4a16_moe_prepare_h(shape, T, topk, hs[0], bufs[0]["sorted_token_ids"], bufs[0]["num_tokens_post_padded"],
+                              bm, scratch)
+        for k in range(len(sets)):
+            next(marks).record()
+            gemm("down", k)
+        next(marks).record()
         w.w4a16_moe_combine(shape, ids, wts, y, out)
-        ev[6].record()
+        next(marks).record()
 
     def forward_step(ev):
         ev[0].record()
-        align()
-        w.w4a16_moe_forward(shape, x, ids, wts, buf["sorted_token_ids"], buf["expert_ids"],
-                            buf["num_tokens_post_padded"], bm, w13p, w2p, out, ws)
+        if args.block_m:
+            align()
+            buf = bufs[0]
+            w.w4a16_moe_forward(shape, x, ids, wts, buf["sorted_token_ids"], buf["expert_ids"],
+                                buf["num_tokens_post_padded"], bm, w13p, w2p, out, ws)
+        else:
+            w.w4a16_moe_routed_forward(shape, x, ids, wts, Eg, w13p, w2p, out, ws)
         ev[1].record()
 
     mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -330,15 +357,16 @@ def main():
     forward_step(mk(2))
     torch.cuda.synchronize()
     ref = out.clone()
-    stages(mk(7))
+    nev = len(names) + 1
+    stages(mk(nev))
     torch.cuda.synchronize()
-    assert torch.equal(ref, out), "staged sequence differs from w4a16_moe_forward"
+    assert torch.equal(ref, out), "staged sequence differs from the one-call layer"
 
     for _ in range(args.warmup):
         if not args.warm:
             flush()
         forward_step(mk(2))
-        stages(mk(7))
+        stages(mk(nev))
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -356,7 +384,7 @@ def main():
     for i in range(args.steps):
         if not args.warm:
             flush()
-        ev = mk(7)
+        ev = mk(nev)
         stages(ev)
         stage_ev.append(ev)
     torch.cuda.synchronize()
@@ -364,14 +392,16 @@ def main():
     route_us = route_align_timing(w, synthetic, dev, c, bm) if not args.no_router else None
 
     layer_us = np.array([a.elapsed_time(b) * 1e3 for a, b in layer_ev])
-    st = np.array([[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(6)] for ev in stage_ev])
+    st = np.array([[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(len(names))] for ev in stage_ev])
     med = float(np.median(layer_us))
     kmed = np.median(st, axis=0)
     work = algorithmic_work(c)
     decode = work["layer_flops"] / max(1, work["layer_bytes"]) < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     layer_gbps = work["layer_bytes"] / (med * 1e-6) / 1e9
     layer_tflops = work["layer_flops"] / (med * 1e-6) / 1e12
-    gate_us = float(kmed[2])
+    kus = {n: round(float(v), 2) for n, v in zip(names, kmed)}
+    # the gate_up step: one kernel, or (split) the heavy-expert tiled kernel then the light-expert stream
+    gate_us = kus["gate_up"] + kus.get("gate_up_light", 0.0)
     if decode:
         achieved = work["gate_up_bytes"] / (gate_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -381,6 +411,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
     roof["kernel"] = gemm_kernel_name(bm, 2 * I, H) + " (gate_up)"
+    if split:
+        roof["kernel"] = (gemm_kernel_name(128, 2 * I, H) + f" (gate_up, experts with >= {split} slots) + "
+                          + gemm_kernel_name(16, 2 * I, H) + " (gate_up, lighter experts)")
     roof["traffic"] = stored_traffic(args.workload, "gate_up")
 
     result = {
@@ -397,15 +430,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": c.name, "T": T, "hidden": H, "intermediate": I, "experts_local": E,
-                   "experts_global": Eg, "topk": topk, "block_m": bm, "resident_slots": work["S"],
+                   "experts_global": Eg, "topk": topk, "block_m": bm if not split else f"128 / 16 split at {split} slots",
+                   "resident_slots": work["S"],
                    "active_experts": work["active"], "cache": "warm" if args.warm else "cold (1 GiB read before each step)"},
         "layer_GBps": round(layer_gbps, 1),
         "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
         "layer_TFLOPs": round(layer_tflops, 2),
         "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
-        "kernels_us": {"align": round(float(kmed[0]), 2), "prepare_x": round(float(kmed[1]), 2),
-                       "gate_up": round(gate_us, 2), "prepare_h": round(float(kmed[3]), 2),
-                       "down": round(float(kmed[4]), 2), "combine": round(float(kmed[5]), 2)},
+        "kernels_us": kus,
         "layer_us_p10_p90": [round(float(np.percentile(layer_us, 10)), 2), round(float(np.percentile(layer_us, 90)), 2)],
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "alg_bytes": work["layer_bytes"],

@@ -10,6 +10,7 @@
  *   moe_align           topk_ids -> sorted_token_ids, expert_ids, num_tokens_post_padded
  *   moe_route_align     router logits -> top-k ids and weights, then moe_align
  *   w4a16_moe_forward   gate_up GEMM + SiLU-and-mul, down GEMM, top-k weighted combine
+ *   w4a16_moe_routed_forward  alignment + the layer in one call, per-expert tile sizes
  *   w4a16_moe_contiguous_forward / w4a16_moe_masked_forward
  *                       the layer on expert-grouped activation layouts
  *   w4a16_repack        once at weight load: canonical int4 + scales -> kernel layout
@@ -144,6 +145,19 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_expe
               int32_t* num_tokens_post_padded, int32_t* expert_counts, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/* moe_align restricted to the experts whose resident slot count c satisfies
+ * min_count <= c <= max_count; the other experts are treated exactly like
+ * ids outside [0, E) (not resident: no slots, no blocks, count 0). Two calls
+ * with complementary ranges split one routing into a light and a heavy set
+ * with their own block_m (per-expert tile sizes for skewed routing: Chord
+ * page, "인덱스 커널 기법", where the tokens-per-expert count picks the block
+ * size). W4A16_ERR_INVALID_ARG for min_count < 0 or max_count < min_count;
+ * otherwise as moe_align. */
+int moe_align_filtered(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t block_m,
+                       int32_t min_count, int32_t max_count, int32_t* sorted_token_ids, int32_t capacity,
+                       int32_t* expert_ids, int32_t* num_tokens_post_padded, int32_t* expert_counts,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Router and alignment in one call: the step in front of the layer, with the
  * outputs of the FlashInfer Kimi-K3 fused router (page "[flashinfer]
  * FlashInfer, B200 GPU에서 Kimi-K3 MoE 라우터 성능 최적화", section "코드 분석":
@@ -262,6 +276,31 @@ int w4a16_moe_down(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const 
                    float* y, void* workspace, size_t workspace_bytes, void* stream);
 int w4a16_moe_combine(const w4a16_moe_shape* shape, int32_t T, int32_t topk, const int32_t* topk_ids,
                       const float* topk_weights, const float* y, uint16_t* out, void* stream);
+
+/* The routed layer in one call, alignment included: topk_ids and weights in,
+ * out written. The block size comes from the tokens-per-expert rule
+ * (w4a16_choose_block_m with num_experts_global). When that rule picks 128
+ * (prefill) the experts are split on the device by their resident count:
+ * experts with at least w4a16_moe_routed_split(...) slots run in 128-row
+ * tiles, lighter ones in 16-row blocks on the weight-streaming GEMMs, so a
+ * skewed routing does not pay a mostly empty 128-row tile for every lightly
+ * used expert (adaptive per-expert tiles; Chord page, "인덱스 커널 기법": the
+ * tile follows the tokens per expert, not the total token count). The result
+ * equals w4a16_moe_forward's up to the fp32 summation inside each GEMM.
+ *
+ *   x, topk_ids, topk_weights, out   as for w4a16_moe_forward
+ *   num_experts_global               experts the router chose among (>= num_experts)
+ *   workspace   device, >= w4a16_moe_routed_workspace_bytes(shape, T, topk, num_experts_global)
+ * Same error codes as w4a16_moe_forward. */
+size_t w4a16_moe_routed_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk,
+                                        int32_t num_experts_global);
+/* The heavy-expert threshold the call uses (slots per expert), 0 when it runs
+ * one alignment, -1 for invalid arguments. */
+int32_t w4a16_moe_routed_split(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t num_experts_global);
+int w4a16_moe_routed_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                             int32_t num_experts_global, const int32_t* topk_ids, const float* topk_weights,
+                             const void* w13_packed, const void* w2_packed, uint16_t* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Expert-grouped activation layouts                                         */

@@ -144,6 +144,23 @@ def test_validation_status_codes(lib):
     assert w.w4a16_moe_masked_block_m(256, 200) == 128
     assert w.w4a16_moe_masked_block_m(48, 4) == 16
     assert w.w4a16_moe_masked_block_m(40, 4) == 0          # not a multiple of 16
+    # filtered alignment and the one-call routed layer
+    assert lib.moe_align_filtered(FAKE, 4, 2, 8, 16, -1, 5, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.moe_align_filtered(FAKE, 4, 2, 8, 16, 6, 5, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.moe_align_filtered(FAKE, 4, 2, 8, 16, 1, 5, FAKE, 10, FAKE, FAKE, None, None, 0, None) == 3
+    kimi = w.make_shape(48, 7168, 2048)
+    assert w.w4a16_moe_routed_split(kimi, 16384, 8, 384) == 32     # prefill: heavy experts from 32 slots
+    assert w.w4a16_moe_routed_split(kimi, 128, 8, 384) == 0        # decode: one alignment
+    assert w.w4a16_moe_routed_split(kimi, 128, 8, 40) == -1        # fewer global than local experts
+    need = w.w4a16_moe_routed_workspace_bytes(kimi, 16384, 8, 384)
+    assert need > w.w4a16_moe_workspace_bytes(kimi, 16384, 8, 128)
+    def rf(T=16384, Eg=384, x=FAKE, ws=FAKE, wsb=need):
+        return lib.w4a16_moe_routed_forward(ctypes.byref(kimi), x, T, 8, Eg, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb,
+                                            None)
+    assert rf(wsb=need - 1) == 4
+    assert rf(x=None) == 1
+    assert rf(Eg=40) == 1
+    assert rf(ws=ctypes.c_void_p(0x1004)) == 1
     # repack and stages
     assert lib.w4a16_repack(ctypes.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.w4a16_moe_combine(ctypes.byref(good), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1

@@ -1,0 +1,143 @@
+"""GPU filtered alignment (moe_align_filtered) and the one-call routed layer
+(w4a16_moe_routed_forward, per-expert tile sizes on skewed routing) vs the oracle:
+a filtered alignment is bit-exact against the oracle's alignment of the same ids
+with the dropped experts marked not resident; the routed layer is within the
+layer tolerance, and equals w4a16_moe_forward bit for bit when it runs one
+alignment."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from _gpu import DeviceCase, parity, say, to_dev
+
+import w4a16_grouped_gemm_amd as w
+
+pytestmark = pytest.mark.gpu
+
+
+def filtered_ids(ids, E, lo, hi):
+    """The oracle side of a count filter: experts with a resident count outside [lo, hi] become -1."""
+    local = (ids >= 0) & (ids < E)
+    cnt = np.bincount(ids[local], minlength=E)
+    drop = (cnt < lo) | (cnt > hi)
+    out = ids.copy()
+    out[local & drop[np.clip(ids, 0, E - 1)]] = -1
+    return out
+
+
+@pytest.mark.parametrize("T,topk,E,bm,lo,hi,seed", [
+    (300, 4, 16, 16, 1, 31, 1),          # single block, light set
+    (300, 4, 16, 128, 32, 2**31 - 1, 1),  # single block, heavy set
+    (5000, 8, 48, 16, 1, 31, 2),         # several chunks, light set
+    (5000, 8, 48, 128, 32, 2**31 - 1, 2),  # several chunks, heavy set
+    (64, 8, 8, 32, 5, 9, 3),             # a band
+])
+def test_align_filtered(T, topk, E, bm, lo, hi, seed):
+    rng = np.random.default_rng(seed)
+    p = rng.zipf(1.3, size=E * 4).astype(np.float64)[:E + 4]
+    ids = np.stack([rng.choice(E + 4, size=topk, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    say(f"align filtered T={T} topk={topk} E={E} bm={bm} range=[{lo},{hi}]")
+    cap = w.moe_align_capacity(T, topk, E, bm)
+    nblk = (cap + bm - 1) // bm
+    s = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    eids = torch.full((nblk,), -7, dtype=torch.int32, device="cuda")
+    ntpp = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    wsb = w.moe_align_workspace_bytes(T, topk, E, bm)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+    w.moe_align_filtered(to_dev(ids), E, bm, lo, hi, s, eids, ntpp, cnt, ws)
+    torch.cuda.synchronize()
+    os_, oe, on, oc = oracle.moe_align(filtered_ids(ids, E, lo, hi), E, bm, capacity=cap)
+    assert int(ntpp.item()) == on
+    np.testing.assert_array_equal(cnt.cpu().numpy(), oc)
+    np.testing.assert_array_equal(s.cpu().numpy(), os_)
+    np.testing.assert_array_equal(eids.cpu().numpy(), oe)
+
+
+def routed(d, Eg, x=None):
+    c = d.case
+    ws = torch.empty(w.w4a16_moe_routed_workspace_bytes(d.shape, c.T, c.topk, Eg), dtype=torch.uint8, device="cuda")
+    out = torch.full((c.T, c.H), -1, dtype=torch.int16, device="cuda")
+    w.w4a16_moe_routed_forward(d.shape, d.x if x is None else x, d.ids, d.wts, Eg, d.w13p, d.w2p, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def test_routed_small_skewed():
+    """An 8-expert slice of 16 routed experts, 64 routed tokens per expert -> block_m 128 and a
+    split: Zipf popularity leaves some local experts heavy and some light."""
+    c = synthetic.random_case("routed_small", T=512, H=256, I=128, E=8, topk=2, block_m=128, seed=33, E_global=16,
+                              logit_bias=synthetic.zipf_bias(16, s=1.5))
+    ids = c.topk_ids
+    cnt = np.bincount(ids[ids < c.E], minlength=c.E)
+    d = DeviceCase(c)
+    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, 16) == 32
+    assert (cnt >= 32).any() and ((cnt > 0) & (cnt < 32)).any(), cnt
+    say(f"routed small: counts {cnt.tolist()}")
+    out = routed(d, 16)
+    ref = oracle.moe_layer(c.x, c.topk_ids, c.topk_weights, c.w13_q, c.w13_s, c.w2_q, c.w2_s, c.E, c.I)
+    parity(out, ref, "routed small skewed")
+    assert np.array_equal(out, routed(d, 16)), "run-to-run difference"
+
+
+def test_routed_graph_replays():
+    """The split call captured in a HIP graph (through torch) and replayed with eager work in
+    between: every replay equals the eager result."""
+    c = synthetic.random_case("routed_graph", T=512, H=256, I=128, E=8, topk=2, block_m=128, seed=34, E_global=16,
+                              logit_bias=synthetic.zipf_bias(16, s=1.5))
+    d = DeviceCase(c)
+    eager = routed(d, 16)
+    ws = torch.empty(w.w4a16_moe_routed_workspace_bytes(d.shape, c.T, c.topk, 16), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((c.T, c.H), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w.w4a16_moe_routed_forward(d.shape, d.x, d.ids, d.wts, 16, d.w13p, d.w2p, out, ws)  # warm-up on s
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        w.w4a16_moe_routed_forward(d.shape, d.x, d.ids, d.wts, 16, d.w13p, d.w2p, out, ws)
+    for i in range(4):
+        out.fill_(-1)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"routed graph replay {i}")
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), eager), f"replay {i} differs"
+        del junk
+
+
+def test_routed_single_alignment_equals_forward():
+    c = synthetic.workload("tiny")
+    d = DeviceCase(c)
+    Eg = c.meta["E_global"]
+    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg) == 0
+    bm = w.w4a16_choose_block_m(c.T, c.topk, c.E, Eg)
+    say(f"routed tiny: block_m {bm}")
+    assert np.array_equal(routed(d, Eg), d.forward(bm))
+
+
+def test_routed_full_size_skewed_sampled():
+    c = synthetic.workload("prefill_skew48")
+    d = DeviceCase(c)
+    Eg = c.meta["E_global"]
+    say(f"routed full-size prefill_skew48: T={c.T} split={w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg)}")
+    out = routed(d, Eg)
+    local = ((c.topk_ids >= 0) & (c.topk_ids < c.E))
+    cnt = np.bincount(c.topk_ids[local], minlength=c.E)
+    # tokens routed to the heaviest expert, to light experts only, and to none
+    heavy_e, light_e = int(np.argmax(cnt)), [e for e in range(c.E) if 0 < cnt[e] < 32]
+    rng = np.random.default_rng(7)
+    pick = set(np.nonzero((c.topk_ids == heavy_e).any(axis=1))[0][:4].tolist())
+    for e in light_e[:6]:
+        pick |= set(np.nonzero((c.topk_ids == e).any(axis=1))[0][:1].tolist())
+    none = np.nonzero(local.sum(axis=1) == 0)[0]
+    pick |= set(none[:2].tolist()) | set(rng.choice(c.T, size=4, replace=False).tolist())
+    tokens = np.array(sorted(pick), np.int32)
+    ref = oracle.moe_layer(c.x, c.topk_ids, c.topk_weights, c.w13_q, c.w13_s, c.w2_q, c.w2_s, c.E, c.I,
+                           tokens=tokens)
+    parity(out[tokens], ref, f"routed prefill_skew48 ({len(tokens)} sampled tokens)")
+    assert np.all(out[none] == 0)

@@ -14,7 +14,8 @@ from ._lib import LIB_PATH, Shape, load
 __all__ = [
     "W4A16Error", "Shape", "LIB_PATH", "load", "make_shape", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "moe_align_capacity", "moe_align_workspace_bytes", "w4a16_choose_block_m", "moe_align",
-    "moe_route_align", "w4a16_moe_contiguous_workspace_bytes", "w4a16_moe_contiguous_forward",
+    "moe_route_align", "moe_align_filtered", "w4a16_moe_routed_workspace_bytes", "w4a16_moe_routed_split",
+    "w4a16_moe_routed_forward", "w4a16_moe_contiguous_workspace_bytes", "w4a16_moe_contiguous_forward",
     "w4a16_moe_masked_block_m", "w4a16_moe_masked_workspace_bytes", "w4a16_moe_masked_forward",
     "w4a16_moe_stage_workspace_bytes", "w4a16_moe_prepare_x", "w4a16_moe_prepare_h",
     "w4a16_moe_workspace_bytes", "w4a16_moe_forward", "w4a16_moe_gate_up", "w4a16_moe_down",
@@ -122,6 +123,31 @@ def w4a16_moe_masked_forward(shape: Shape, x, masked_m, block_m: int, w13_packed
     _check(load().w4a16_moe_masked_forward(ctypes.byref(shape), _p(x), max_m, _p(masked_m), block_m,
                                            _p(w13_packed), _p(w2_packed), _p(out), _p(workspace),
                                            _nbytes(workspace), _stream(stream)), "w4a16_moe_masked_forward")
+
+
+def moe_align_filtered(topk_ids, num_experts: int, block_m: int, min_count: int, max_count: int, sorted_token_ids,
+                       expert_ids, num_tokens_post_padded, expert_counts=None, workspace=None, stream=None):
+    T, topk = topk_ids.shape
+    _check(load().moe_align_filtered(_p(topk_ids), T, topk, num_experts, block_m, min_count, max_count,
+                                     _p(sorted_token_ids), sorted_token_ids.numel(), _p(expert_ids),
+                                     _p(num_tokens_post_padded), _p(expert_counts), _p(workspace), _nbytes(workspace),
+                                     _stream(stream)), "moe_align_filtered")
+
+
+def w4a16_moe_routed_workspace_bytes(shape: Shape, T: int, topk: int, num_experts_global: int) -> int:
+    return load().w4a16_moe_routed_workspace_bytes(ctypes.byref(shape), T, topk, num_experts_global)
+
+
+def w4a16_moe_routed_split(shape: Shape, T: int, topk: int, num_experts_global: int) -> int:
+    return load().w4a16_moe_routed_split(ctypes.byref(shape), T, topk, num_experts_global)
+
+
+def w4a16_moe_routed_forward(shape: Shape, x, topk_ids, topk_weights, num_experts_global: int, w13_packed, w2_packed,
+                             out, workspace, stream=None):
+    T, topk = topk_ids.shape
+    _check(load().w4a16_moe_routed_forward(ctypes.byref(shape), _p(x), T, topk, num_experts_global, _p(topk_ids),
+                                           _p(topk_weights), _p(w13_packed), _p(w2_packed), _p(out), _p(workspace),
+                                           _nbytes(workspace), _stream(stream)), "w4a16_moe_routed_forward")
 
 
 def w4a16_moe_workspace_bytes(shape: Shape, T: int, topk: int, block_m: int) -> int:

@@ -111,13 +111,20 @@ __device__ __forceinline__ void count_ids(const int (&v)[kPerThread], int E, int
 // Wave 0 writes off[0..E] = exclusive prefix of padded counts (off[E] = the
 // padded total), cursor[e] = off[e] (+ the old cursor[e] when add_cursor), and,
 // where the pointers are not null, the counts and the padded total to global
-// memory. Lane l owns experts [l * per, (l + 1) * per), held in registers; one
+// memory. An expert whose count lies outside `keep` is dropped: its count
+// becomes 0 (in LDS too, which the scatter reads) and its ids are skipped. Lane l owns experts [l * per, (l + 1) * per), held in registers; one
 // DPP wave scan. E <= 64 * kMaxExpertsPerLane.
 constexpr int kMaxExpertsPerLane = 8;
+
+// Experts kept by an alignment: those with lo <= count <= hi.
+struct CountRange {
+  int lo, hi;
+};
+constexpr CountRange kAllCounts = {0, 0x7fffffff};
 static_assert(64 * kMaxExpertsPerLane >= W4A16_MAX_EXPERTS, "one scan wave must hold every expert");
 
-__device__ void scan_offsets(const int* counts, int E, int bm, int* off, int* cursor, bool add_cursor,
-                             int32_t* __restrict__ counts_out, int32_t* __restrict__ ntpp_out) {
+__device__ void scan_offsets(int* counts, int E, int bm, int* off, int* cursor, bool add_cursor,
+                             int32_t* __restrict__ counts_out, int32_t* __restrict__ ntpp_out, CountRange keep) {
   if (threadIdx.x < 64) {
     const int lane = (int)threadIdx.x;
     const int per = (E + 63) / 64;
@@ -127,6 +134,7 @@ __device__ void scan_offsets(const int* counts, int E, int bm, int* off, int* cu
 #pragma unroll
     for (int k = 0; k < kMaxExpertsPerLane; ++k) {
       c[k] = (k < per && start + k < E) ? counts[start + k] : 0;
+      if (c[k] < keep.lo || c[k] > keep.hi) c[k] = 0;  // an expert outside the range is not resident
       local += padded(c[k], bm);
     }
     const int incl = wave_incl_scan(local);
@@ -135,6 +143,7 @@ __device__ void scan_offsets(const int* counts, int E, int bm, int* off, int* cu
     for (int k = 0; k < kMaxExpertsPerLane; ++k) {
       const int e = start + k;
       if (k < per && e < E) {
+        counts[e] = c[k];
         off[e] = run;
         cursor[e] = (add_cursor ? cursor[e] : 0) + run;
         if (counts_out) counts_out[e] = c[k];
@@ -197,8 +206,8 @@ __device__ void fill_tail(int ntpp, int bm, int32_t* sorted, int capacity, int32
 // below), so the steps need no workgroup barrier. The 16 per-wave counts of an
 // expert are then turned into per-wave bases by one 16-lane row scan. wcnt is
 // LDS scratch of kWaves * E ints, zeroed by the caller before its last barrier.
-__device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nbits, const int* cursor, int* wcnt,
-                            int32_t* __restrict__ sorted, int capacity, int lo) {
+__device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nbits, const int* counts,
+                            const int* cursor, int* wcnt, int32_t* __restrict__ sorted, int capacity, int lo) {
   const int wave = (int)threadIdx.x >> 6;
   int* row = wcnt + wave * E;
   int rank[kPerThread];
@@ -207,7 +216,7 @@ __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nb
     rank[r] = 0;
     if (r < steps) {  // uniform
       const int e = v[r];
-      const bool local = (unsigned)e < (unsigned)E;
+      const bool local = (unsigned)e < (unsigned)E && counts[e] > 0;  // resident and kept
       uint64_t peers = __ballot(local);
       for (int b = 0; b < nbits; ++b) {
         const bool bit = (e >> b) & 1;
@@ -231,7 +240,7 @@ __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nb
   lds_barrier();  // per-wave bases visible
 #pragma unroll
   for (int r = 0; r < kPerThread; ++r)
-    if (r < steps && (unsigned)v[r] < (unsigned)E) {
+    if (r < steps && (unsigned)v[r] < (unsigned)E && counts[v[r]] > 0) {
       const int pos = row[v[r]] + rank[r];  // < capacity: the capacity covers every padded count
       if ((unsigned)pos < (unsigned)capacity) sorted[pos] = id_index(lo, steps, r);
     }
@@ -242,7 +251,7 @@ __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nb
 // one block. LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
 __device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, int* smem, int32_t* __restrict__ sorted,
                             int capacity, int32_t* __restrict__ expert_ids, int nblk, int32_t* __restrict__ ntpp_out,
-                            int32_t* __restrict__ counts_out) {
+                            int32_t* __restrict__ counts_out, CountRange keep) {
   int* counts = smem;
   int* off = counts + E;
   int* cursor = off + E + 1;
@@ -253,25 +262,25 @@ __device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, in
   lds_barrier();
   count_ids(v, E, counts);
   lds_barrier();
-  scan_offsets(counts, E, bm, off, cursor, false, counts_out, ntpp_out);
+  scan_offsets(counts, E, bm, off, cursor, false, counts_out, ntpp_out, keep);
   lds_barrier();
   const int ntpp = off[E];
   label_blocks(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, (int)threadIdx.x >> 4,
                kThreads / 16);
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, (int)threadIdx.x, kThreads);
   lds_barrier();
-  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, capacity, 0);
+  scatter_ids(v, steps, E, id_bits(E), counts, cursor, wtab, sorted, capacity, 0);
 }
 
 __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
                                                                int32_t* __restrict__ sorted, int capacity,
                                                                int32_t* __restrict__ expert_ids, int nblk,
                                                                int32_t* __restrict__ ntpp_out,
-                                                               int32_t* __restrict__ counts_out) {
+                                                               int32_t* __restrict__ counts_out, CountRange keep) {
   extern __shared__ int smem[];
   int v[kPerThread];
   load_ids(ids, 0, n, block_steps(0, n), v);
-  align_block(v, n, E, bm, smem, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out);
+  align_block(v, n, E, bm, smem, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out, keep);
 }
 
 // ---- multi-block path -------------------------------------------------------
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
                                                                  int32_t* __restrict__ sorted, int capacity,
                                                                  int32_t* __restrict__ expert_ids, int nblk,
                                                                  int32_t* __restrict__ ntpp_out,
-                                                                 int32_t* __restrict__ counts_out) {
+                                                                 int32_t* __restrict__ counts_out, CountRange keep) {
   extern __shared__ int smem[];
   int* counts = smem;
   int* off = counts + E;
@@ -323,14 +332,14 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
   }
   lds_barrier();
   scan_offsets(counts, E, bm, off, cursor, true, blockIdx.x == 0 ? counts_out : nullptr,
-               blockIdx.x == 0 ? ntpp_out : nullptr);
+               blockIdx.x == 0 ? ntpp_out : nullptr, keep);
   lds_barrier();
   const int ntpp = off[E];
   const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
   label_blocks(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, gt >> 4, gstep / 16);
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, gt, gstep);
   lds_barrier();
-  scatter_ids(v, steps, E, id_bits(E), cursor, wtab, sorted, capacity, lo);
+  scatter_ids(v, steps, E, id_bits(E), counts, cursor, wtab, sorted, capacity, lo);
 }
 
 // T == 0: every output is a sentinel.
@@ -510,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void route_align_small_kernel(
     const int i = id_index(0, 1, r);  // n <= kThreads: one step
     v[r] = (r == 0 && i < n) ? ids[i] : -1;
   }
-  align_block(v, n, E, bm, smem + kFusedIds, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out);
+  align_block(v, n, E, bm, smem + kFusedIds, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out, kAllCounts);
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -526,8 +535,10 @@ size_t align_workspace_bytes(int64_t n, int32_t E) {
 }
 
 hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, int32_t* sorted, int32_t capacity,
-                        int32_t* expert_ids, int32_t* ntpp, int32_t* counts, void* workspace, hipStream_t stream) {
+                        int32_t* expert_ids, int32_t* ntpp, int32_t* counts, void* workspace, hipStream_t stream,
+                        int32_t min_count, int32_t max_count, bool reuse_hist) {
   const int nblk = (capacity + bm - 1) / bm;
+  const CountRange keep = {min_count, max_count};
   if (n == 0) {
     const int grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, ((int64_t)capacity + 255) / 256));
     hipLaunchKernelGGL(align_empty_kernel, dim3(grid), dim3(256), 0, stream, sorted, capacity, n, expert_ids, nblk,
@@ -536,17 +547,19 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, in
   }
   if (n <= kSmallMax) {
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, sorted,
-                       capacity, expert_ids, nblk, ntpp, counts);
+                       capacity, expert_ids, nblk, ntpp, counts, keep);
     return hipGetLastError();
   }
   const int nchunks = (n + kChunk - 1) / kChunk;
   int* hist = static_cast<int*>(workspace);
-  hipLaunchKernelGGL(align_hist_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, stream, ids, n, E,
-                     hist);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (!reuse_hist) {
+    hipLaunchKernelGGL(align_hist_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, stream, ids, n, E,
+                       hist);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, hist,
-                     nchunks, sorted, capacity, expert_ids, nblk, ntpp, counts);
+                     nchunks, sorted, capacity, expert_ids, nblk, ntpp, counts, keep);
   return hipGetLastError();
 }
 

@@ -135,15 +135,25 @@ int32_t w4a16_choose_block_m(int32_t T, int32_t topk, int32_t num_experts_local,
 int moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t block_m,
               int32_t* sorted_token_ids, int32_t capacity, int32_t* expert_ids, int32_t* num_tokens_post_padded,
               int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_align_filtered(topk_ids, T, topk, num_experts, block_m, 0, INT32_MAX, sorted_token_ids, capacity,
+                            expert_ids, num_tokens_post_padded, expert_counts, workspace, workspace_bytes, stream);
+}
+
+int moe_align_filtered(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t block_m,
+                       int32_t min_count, int32_t max_count, int32_t* sorted_token_ids, int32_t capacity,
+                       int32_t* expert_ids, int32_t* num_tokens_post_padded, int32_t* expert_counts, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   const int st = check_tokens(T, topk, num_experts, block_m);
   if (st != W4A16_OK) return st;
+  if (min_count < 0 || max_count < min_count) return W4A16_ERR_INVALID_ARG;
   if ((T > 0 && !topk_ids) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
     return W4A16_ERR_INVALID_ARG;
   if (capacity < 0 || (size_t)capacity < moe_align_capacity(T, topk, num_experts, block_m)) return W4A16_ERR_CAPACITY;
   const size_t ws = align_workspace_bytes((int64_t)T * topk, num_experts);
   if (ws > 0 && (!workspace || workspace_bytes < ws)) return W4A16_ERR_WORKSPACE;
   return hip_status(launch_align(topk_ids, T * topk, num_experts, block_m, sorted_token_ids, capacity, expert_ids,
-                                 num_tokens_post_padded, expert_counts, workspace, static_cast<hipStream_t>(stream)));
+                                 num_tokens_post_padded, expert_counts, workspace, static_cast<hipStream_t>(stream),
+                                 min_count, max_count));
 }
 
 int moe_route_align(const float* logits, const float* bias, int32_t T, int32_t num_routed_experts, int32_t topk,
@@ -453,6 +463,146 @@ int w4a16_moe_masked_forward(const w4a16_moe_shape* shape, const uint16_t* x, in
   if ((M > 0 && (!x || !masked_m || !out)) || !w13_packed || !w2_packed) return W4A16_ERR_INVALID_ARG;
   return grouped_forward(kMasked, shape, x, (int32_t)M, max_m, nullptr, masked_m, block_m, w13_packed, w2_packed,
                          out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// The routed layer in one call. Prefill-sized calls on an expert slice
+// (block_m 128 by the tokens-per-expert rule, tiled GEMMs available, fewer
+// local than routed experts, so the local counts can be very uneven) split the
+// experts by their resident count: experts with at least kHeavyRows slots run
+// in 128-row tiles on the MFMA-bound tiled GEMMs, the lighter ones in 16-row
+// blocks on the weight-streaming GEMMs, so a light expert no longer pays for a
+// mostly empty 128-row tile. Other calls use one alignment at the rule's
+// block_m. (Running the light set on a second stream, next to the heavy
+// tiles, was measured: both kernels slowed down by about what they overlapped,
+// so the sets run one after the other on the caller's stream.)
+constexpr int32_t kHeavyRows = 32;
+constexpr int32_t kLightBlockM = 16;
+constexpr int32_t kHeavyBlockM = 128;
+
+struct AlignSet {
+  size_t sorted, expert_ids, ntpp, h;
+  int32_t block_m, capacity;
+};
+
+struct RoutedWorkspace {
+  bool split;
+  AlignSet set[2];  // [0]: the only set, or the heavy set; [1]: the light set
+  size_t hist, y, scratch, scratch_bytes, total;
+};
+
+RoutedWorkspace routed_workspace(const w4a16_moe_shape* s, int32_t T, int32_t topk, int32_t num_experts_global) {
+  RoutedWorkspace r{};
+  const int32_t E = s->num_experts, H = s->hidden, I = s->intermediate;
+  const int32_t bm = w4a16_choose_block_m(T, topk, E, num_experts_global);
+  r.split = bm == kHeavyBlockM && tiled_gemm_supported(kHeavyBlockM, 2 * I, H) && num_experts_global > E;
+  const int nsets = r.split ? 2 : 1;
+  r.set[0].block_m = r.split ? kHeavyBlockM : bm;
+  r.set[1].block_m = kLightBlockM;
+  size_t off = 0;
+  r.hist = off;
+  off += round_up(align_workspace_bytes((int64_t)T * topk, E));
+  for (int k = 0; k < nsets; ++k) {
+    AlignSet& a = r.set[k];
+    a.capacity = (int32_t)moe_align_capacity(T, topk, E, a.block_m);
+    // a light expert holds fewer than kHeavyRows slots: at most kHeavyRows rows once padded
+    if (k == 1) a.capacity = std::min<int32_t>(a.capacity, E * kHeavyRows);
+    a.sorted = off;
+    off += round_up((size_t)a.capacity * 4);
+    a.expert_ids = off;
+    off += round_up(((size_t)a.capacity + a.block_m - 1) / a.block_m * 4);
+    a.ntpp = off;
+    off += kAlign;
+    a.h = off;
+    off += round_up((size_t)a.capacity * I * 2);
+  }
+  r.y = off;
+  off += round_up((size_t)T * topk * H * 4);
+  r.scratch = off;
+  r.scratch_bytes = w4a16_moe_stage_workspace_bytes(s, T, topk, r.set[0].block_m);
+  r.total = off + r.scratch_bytes;
+  return r;
+}
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_moe_routed_workspace_bytes(const w4a16_moe_shape* shape, int32_t T, int32_t topk,
+                                        int32_t num_experts_global) {
+  if (check_shape(shape) != W4A16_OK || num_experts_global < shape->num_experts) return 0;
+  if (check_tokens(T, topk, shape->num_experts, kHeavyBlockM) != W4A16_OK) return 0;
+  return routed_workspace(shape, T, topk, num_experts_global).total;
+}
+
+int32_t w4a16_moe_routed_split(const w4a16_moe_shape* shape, int32_t T, int32_t topk, int32_t num_experts_global) {
+  if (check_shape(shape) != W4A16_OK || num_experts_global < shape->num_experts) return -1;
+  if (check_tokens(T, topk, shape->num_experts, kHeavyBlockM) != W4A16_OK) return -1;
+  return routed_workspace(shape, T, topk, num_experts_global).split ? kHeavyRows : 0;
+}
+
+int w4a16_moe_routed_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                             int32_t num_experts_global, const int32_t* topk_ids, const float* topk_weights,
+                             const void* w13_packed, const void* w2_packed, uint16_t* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != W4A16_OK) return st;
+  if (num_experts_global < shape->num_experts) return W4A16_ERR_INVALID_ARG;
+  st = check_tokens(T, topk, shape->num_experts, kHeavyBlockM);  // the largest capacity any set uses
+  if (st != W4A16_OK) return st;
+  if ((T > 0 && (!x || !topk_ids || !topk_weights || !out)) || !w13_packed || !w2_packed)
+    return W4A16_ERR_INVALID_ARG;
+  if (!all_aligned16(x, out, w13_packed, w2_packed, workspace)) return W4A16_ERR_INVALID_ARG;
+  const RoutedWorkspace r = routed_workspace(shape, T, topk, num_experts_global);
+  if (!workspace || workspace_bytes < r.total) return W4A16_ERR_WORKSPACE;
+  if (T == 0) return W4A16_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int32_t E = shape->num_experts;
+  const int nsets = r.split ? 2 : 1;
+  int32_t* sorted[2];
+  int32_t* eids[2];
+  int32_t* ntpp[2];
+  uint16_t* h[2];
+  for (int k = 0; k < nsets; ++k) {
+    sorted[k] = reinterpret_cast<int32_t*>(ws + r.set[k].sorted);
+    eids[k] = reinterpret_cast<int32_t*>(ws + r.set[k].expert_ids);
+    ntpp[k] = reinterpret_cast<int32_t*>(ws + r.set[k].ntpp);
+    h[k] = reinterpret_cast<uint16_t*>(ws + r.set[k].h);
+  }
+  float* y = reinterpret_cast<float*>(ws + r.y);
+  void* scratch = ws + r.scratch;
+  void* hist = ws + r.hist;
+  // alignments: the heavy set (or the only one), then the light set over the same histograms
+  for (int k = 0; k < nsets; ++k) {
+    const int32_t lo = !r.split ? 0 : (k == 0 ? kHeavyRows : 1);
+    const int32_t hi = !r.split ? INT32_MAX : (k == 0 ? INT32_MAX : kHeavyRows - 1);
+    st = hip_status(launch_align(topk_ids, T * topk, E, r.set[k].block_m, sorted[k], r.set[k].capacity, eids[k],
+                                 ntpp[k], nullptr, hist, hs, lo, hi, k > 0));
+    if (st != W4A16_OK) return st;
+  }
+  st = w4a16_moe_prepare_x(shape, x, T, topk, topk_ids, r.set[0].block_m, scratch, r.scratch_bytes, stream);
+  if (st != W4A16_OK) return st;
+  const int32_t H = shape->hidden, I = shape->intermediate;
+  // the light set's capacity is below moe_align_capacity, so its GEMMs are launched here directly
+  const auto gemm = [&](GemmMode mode, int k) {
+    const bool up = mode == kGateUp;
+    GemmParams p = gemm_params(shape, T, topk, sorted[k], r.set[k].capacity, eids[k], ntpp[k],
+                               up ? w13_packed : w2_packed, up ? 2 * I : H, up ? H : I);
+    p.a = up ? x : h[k];
+    p.out = up ? static_cast<void*>(h[k]) : static_cast<void*>(y);
+    p.out_ld = up ? I : H;
+    return hip_status(launch_moe_gemm(mode, r.set[k].block_m, p, scratch, hs));
+  };
+  for (int k = 0; k < nsets; ++k)
+    if ((st = gemm(kGateUp, k)) != W4A16_OK) return st;
+  st = w4a16_moe_prepare_h(shape, T, topk, h[0], sorted[0], r.set[0].capacity, ntpp[0], r.set[0].block_m, scratch,
+                           r.scratch_bytes, stream);
+  if (st != W4A16_OK) return st;
+  for (int k = 0; k < nsets; ++k)
+    if ((st = gemm(kDown, k)) != W4A16_OK) return st;
+  return w4a16_moe_combine(shape, T, topk, topk_ids, topk_weights, y, out, stream);
 }
 
 }  // extern "C"
