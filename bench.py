@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the W4A16 fused MoE layer on one MI355X.
 
-One step = one pass of the whole layer over one batch of synthetic input:
-moe_align, then gate_up + SiLU-and-mul, down, and the top-k combine (the
-w4a16_moe_forward sequence). Inputs and repacked weights are resident in HBM
-before timing starts; weight repack is load time and is not timed.
+One step = one pass of the whole layer over one batch of synthetic input: one
+call of w4a16_moe_routed_forward, i.e. the alignment, gate_up + SiLU-and-mul,
+down and the top-k combine (with per-expert tile sizes on skewed prefill).
+Inputs and repacked weights are resident in HBM before timing starts; weight
+repack is load time and is not timed. A staged replica of the same path gives
+the per-kernel breakdown.
 
 Timing follows the pages' kernel-benchmark method (Humming announcement,
 "Humming: vLLM과 Ant Group, 양자화 추론을 위한 범용 커널 라이브러리 오픈소스 공개",
