@@ -53,6 +53,16 @@ def test_align_path_boundaries(n_ids):
     check(ids, 64, 32, what=f"boundary {n_ids}")
 
 
+@pytest.mark.parametrize("n_ids,E,bm", [(1, 1, 16), (2, 48, 16), (8, 48, 128), (63, 512, 16), (64, 7, 32),
+                                         (64, 512, 64), (65, 48, 16)])
+def test_align_one_wave_path(n_ids, E, bm):
+    """Up to 64 ids one wave aligns them (the path the fused router uses for up to 8 tokens of top-8)."""
+    rng = np.random.default_rng(n_ids * 1000 + E)
+    ids = rng.integers(-2, E + 3, size=(n_ids, 1)).astype(np.int32)
+    ids[: n_ids // 2] = rng.integers(0, max(1, E // 4), size=(n_ids // 2, 1))  # repeated experts
+    check(ids, E, bm, what=f"one-wave n={n_ids}")
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_align_fuzz(seed):
     rng = np.random.default_rng(1000 + seed)

@@ -272,12 +272,64 @@ __device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, in
   scatter_ids(v, steps, E, id_bits(E), counts, cursor, wtab, sorted, capacity, 0);
 }
 
+// The alignment of n <= 64 ids by wave 0 alone (lane i holds id i in v0, -1
+// past n). The caller has already zeroed counts[E] in LDS and filled the whole
+// of sorted with the sentinel n and expert_ids with -1, and has passed a
+// __syncthreads() since (it orders those stores before the ones here). The
+// wave ranks, counts, scans (its LDS accesses run in order: no barrier), then
+// writes the resident ids and labels its used blocks; padding and tail are
+// already right. LDS: counts[E], off[E+1], cursor[E].
+constexpr int kWaveMax = 64;
+
+__device__ void prefill_outputs(int E, int32_t* __restrict__ sorted, int capacity, int32_t* __restrict__ expert_ids,
+                                int nblk, int sentinel, int* counts) {
+  for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = 0;
+  for (int p = (int)threadIdx.x; p < capacity; p += kThreads) sorted[p] = sentinel;
+  for (int b = (int)threadIdx.x; b < nblk; b += kThreads) expert_ids[b] = -1;
+}
+
+__device__ void align_wave(int v0, int E, int bm, int* smem, int32_t* __restrict__ sorted, int capacity,
+                           int32_t* __restrict__ expert_ids, int nblk, int32_t* __restrict__ ntpp_out,
+                           int32_t* __restrict__ counts_out, CountRange keep) {
+  if (threadIdx.x >= 64) return;
+  int* counts = smem;
+  int* off = counts + E;
+  int* cursor = off + E + 1;
+  const int lane = (int)threadIdx.x;
+  const int e = v0;
+  const bool local = (unsigned)e < (unsigned)E;
+  uint64_t peers = __ballot(local);
+  const int nbits = id_bits(E);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(local && bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank = rank_below(peers);  // resident ids of e in lanes below: the stable order
+  if (local && rank == 0) counts[e] = __popcll(peers);
+  scan_offsets(counts, E, bm, off, cursor, false, counts_out, ntpp_out, keep);
+  if (local && counts[e] > 0) {  // kept by the count range
+    const int base = off[e];
+    const int pos = base + rank;
+    if ((unsigned)pos < (unsigned)capacity) sorted[pos] = lane;
+    if (rank == 0)  // the expert's leader labels its blocks
+      for (int b = base / bm; b < min((base + padded(counts[e], bm)) / bm, nblk); ++b) expert_ids[b] = e;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
                                                                int32_t* __restrict__ sorted, int capacity,
                                                                int32_t* __restrict__ expert_ids, int nblk,
                                                                int32_t* __restrict__ ntpp_out,
                                                                int32_t* __restrict__ counts_out, CountRange keep) {
   extern __shared__ int smem[];
+  if (n <= kWaveMax) {  // uniform
+    const int v0 = threadIdx.x < (unsigned)n ? ids[threadIdx.x] : -1;
+    prefill_outputs(E, sorted, capacity, expert_ids, nblk, n, smem);
+    __syncthreads();  // also waits for the prefill stores
+    align_wave(v0, E, bm, smem, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out, keep);
+    return;
+  }
   int v[kPerThread];
   load_ids(ids, 0, n, block_steps(0, n), v);
   align_block(v, n, E, bm, smem, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out, keep);
@@ -507,12 +559,20 @@ __global__ __launch_bounds__(kThreads) void route_align_small_kernel(
   extern __shared__ int smem[];
   int* ids = smem;
   const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int n = T * topk;
+  // up to 64 ids: the output prefill runs while the waves route
+  if (n <= kWaveMax) prefill_outputs(E, sorted, capacity, expert_ids, nblk, n, smem + kFusedIds);
   if (wave < T) {
     const int id = route_token<SLOTS>(logits, bias, wave, Eg, topk, topk_ids, topk_weights);
     if (lane < topk) ids[wave * topk + lane] = id;
   }
+  if (n <= kWaveMax) {  // uniform
+    __syncthreads();  // ids in LDS, and the prefill stores done
+    const int v0 = threadIdx.x < (unsigned)n ? ids[threadIdx.x] : -1;
+    align_wave(v0, E, bm, smem + kFusedIds, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out, kAllCounts);
+    return;
+  }
   lds_barrier();
-  const int n = T * topk;
   int v[kPerThread];
 #pragma unroll
   for (int r = 0; r < kPerThread; ++r) {
