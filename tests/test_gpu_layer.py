@@ -43,6 +43,10 @@ SMALL = [
     ("short K bm16", 64, 1024, 256, 8, 2, 8, 16),
     ("short K bm32", 64, 1024, 256, 8, 2, 8, 32),
     ("short K bm64", 200, 1024, 256, 4, 2, 4, 64),
+    # long reductions at block_m 16: two waves split each n-block's K (gate_up K = 2048; down K = 2048)
+    ("split K gate_up", 40, 2048, 128, 8, 2, 16, 16),
+    ("split K down", 40, 256, 2048, 8, 2, 16, 16),
+    ("split K both, ragged", 9, 2304, 2304, 6, 3, 6, 16),
 ]
 
 

@@ -120,9 +120,13 @@ __device__ __forceinline__ void store_nblock(const GemmParams& p, floatx4 (&acc)
     for (int c = 0; c < 4; ++c) acc[rb][c] = zero4;
 }
 
-template <int RB, int U, int DEPTH>
+// KS: waves per n-block. KS = 2 splits each n-block's reduction between two
+// waves of the workgroup (groups [0, G/2) and [G/2, G)); a unit then covers 2
+// n-blocks, so a call has twice the units, and the two partial sums meet in
+// LDS at the end of the unit (added in that fixed order: deterministic).
+template <int RB, int U, int DEPTH, int KS = 1>
 struct Cfg {
-  static constexpr int kABlocks = RB * U;                 // 1 KiB A fragments per batch
+  static constexpr int kABlocks = KS * RB * U;            // 1 KiB A fragments per batch (both halves)
   static constexpr int kACopiesPerWave = kABlocks / 4;    // spread over the 4 waves
   static constexpr int kSCopies = U / 2;                  // 256-byte scale copies per wave per batch
   static constexpr int kOpsPerBatch = kACopiesPerWave + kSCopies + U;
@@ -139,11 +143,11 @@ struct Cfg {
 // so a wait for the nibbles also covers the copies).
 // a_slot < 0: the A fragments of this batch are already resident (short K,
 // see the kernel); otherwise they are copied into A slot a_slot.
-template <int RB, int U, int DEPTH>
+template <int RB, int U, int DEPTH, int KS>
 __device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int a_slot, int b, int G, int wave,
                                             const uint8_t* const* a_src,
                                             const uint8_t* ws, const uint8_t* wq, uint8_t* a_ring, uint8_t* s_ring) {
-  using C = Cfg<RB, U, DEPTH>;
+  using C = Cfg<RB, U, DEPTH, KS>;
   int g0 = b * U;
   asm volatile("" : "+s"(g0));  // keep the look-ahead where it is written
   const int ga = g0 % G;        // the A rows cycle through K once per n-block
@@ -169,9 +173,10 @@ __device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int a_slo
 // long-K kernel's register count where it was. With MULTI and K / 32 <= U x DEPTH
 // groups the row block's A fragments for the whole of K fit the A ring: they
 // are copied during the first n-block only and stay resident for the others.
-template <int MODE, int RB, int U, int DEPTH, bool MULTI>
+template <int MODE, int RB, int U, int DEPTH, bool MULTI, int KS>
 __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p, int KN) {
-  using C = Cfg<RB, U, DEPTH>;
+  static_assert(KS == 1 || (KS == 2 && !MULTI), "a split reduction runs one n-block per wave");
+  using C = Cfg<RB, U, DEPTH, KS>;
   constexpr int BM = 16 * RB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = (int)threadIdx.x & 63;
@@ -183,10 +188,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
   const int ntpp = min(*p.ntpp, p.capacity);
   const int n_mblocks = ntpp / BM;
   const int NB = p.N / kNBlock;
-  const int NG = NB / (kUnitNBlocks * KN);  // units per row block
+  const int NG = NB / (kUnitNBlocks / KS * KN);  // units per row block
   const int G = p.K / kGroup;
-  const int nbatch = KN * G / U;            // batches per wave per unit
-  const int kbatch = G / U;                 // batches per n-block
+  const int Gw = G / KS;                    // groups of one n-block this wave reduces
+  const int kh = KS == 2 ? (wave & 1) : 0;  // which part of K
+  const int nbatch = KN * Gw / U;           // batches per wave per unit
+  const int kbatch = Gw / U;                // batches per n-block
   const bool a_resident = MULTI && kbatch <= DEPTH;
   const int units = n_mblocks * NG;
   const int per_wg = (units + (int)gridDim.x - 1) / (int)gridDim.x;
@@ -202,16 +209,18 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
     const int ng = unit - mb * NG;
     const int e = p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
-    const int nb0 = (ng * kUnitNBlocks + wave) * KN;  // this wave's first n-block
+    const int nb0 = (ng * (kUnitNBlocks / KS) + wave / KS) * KN;  // this wave's first n-block
 
     // A copy sources: this wave copies fragment blocks j = wave + 4 t of each
-    // batch, block j = (row block j / U, group j % U). Padding rows read the
-    // row block's first row; their results are never stored.
+    // batch, block j = (part of K j / (RB U), row block, group); the part
+    // offsets the source by Gw groups. Padding rows read the row block's first
+    // row; their results are never stored.
     const uint8_t* a_src[C::kACopiesPerWave];
 #pragma unroll
     for (int t = 0; t < C::kACopiesPerWave; ++t) {
       const int j = wave + 4 * t;
-      const int rb = j / U, uu = j % U;
+      const int khj = j / (RB * U), jj = j % (RB * U);
+      const int rb = jj / U, uu = jj % U;
       const int prow = mb * BM + rb * 16 + (lane & 15);
       const int id = p.sorted[prow];
       const bool real = (unsigned)id < (unsigned)p.n_slots;
@@ -222,9 +231,10 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
       } else {
         src = real ? prow : mb * BM;
       }
-      a_src[t] = reinterpret_cast<const uint8_t*>(p.a + src * p.K) + 16 * (lane >> 4) + uu * (kGroup * 2);
+      a_src[t] = reinterpret_cast<const uint8_t*>(p.a + src * p.K) + 16 * (lane >> 4) + uu * (kGroup * 2) +
+                 (int64_t)khj * Gw * (kGroup * 2);
     }
-    const int64_t unit0 = ((int64_t)e * NB + nb0) * G;
+    const int64_t unit0 = ((int64_t)e * NB + nb0) * G + (int64_t)kh * Gw;
     const uint8_t* wq = p.wq + unit0 * kNibUnitBytes + 16 * lane;
     const uint8_t* ws = reinterpret_cast<const uint8_t*>(p.ws + unit0 * kScaleUnitElems) + 4 * lane;
 
@@ -247,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
 #pragma unroll
     for (int s = 0; s < DEPTH - 1; ++s)
       if (s < nbatch)
-        issue_batch<RB, U, DEPTH>(nib[s], s, a_resident ? (s < kbatch ? s : -1) : s, s, G, wave, a_src, ws, wq,
-                                  a_ring, s_ring);
+        issue_batch<RB, U, DEPTH, KS>(nib[s], s, a_resident ? (s < kbatch ? s : -1) : s, s, G, wave, a_src, ws,
+                                      wq, a_ring, s_ring);
 
     for (int b0 = 0; b0 < nbatch; b0 += DEPTH) {
 #pragma unroll
@@ -268,10 +278,10 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
           ring_barrier();
           if (b + DEPTH - 1 < nbatch) {
             const int bn = b + DEPTH - 1, sn = (k + DEPTH - 1) % DEPTH;
-            issue_batch<RB, U, DEPTH>(nib[sn], sn, a_resident ? (bn < kbatch ? bn : -1) : sn, bn, G, wave, a_src, ws,
-                                      wq, a_ring, s_ring);
+            issue_batch<RB, U, DEPTH, KS>(nib[sn], sn, a_resident ? (bn < kbatch ? bn : -1) : sn, bn, G, wave, a_src,
+                                          ws, wq, a_ring, s_ring);
           }
-          const uint8_t* abase = a_ring + (a_resident ? b % kbatch : k) * C::kABatchBytes;
+          const uint8_t* abase = a_ring + (a_resident ? b % kbatch : k) * C::kABatchBytes + kh * (RB * U * 1024);
           const uint8_t* sbase = s_ring + k * C::kSBatchBytes;
 #pragma unroll
           for (int uu = 0; uu < U; ++uu) {
@@ -294,7 +304,33 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
         }
       }
     }
-    if (!MULTI) store_nblock<MODE, RB>(p, acc, mem_ids, mb, nb0, lane);
+    if (KS == 2) {
+      // the upper part's wave hands its partial sums to the lower part's wave
+      // through LDS (the rings are free once every wave passed this barrier)
+      ring_barrier();
+      float* xch = reinterpret_cast<float*>(lds) + (wave >> 1) * (RB * 16 * 64);
+      if (kh == 1) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xch[((rb * 4 + c) * 4 + i) * 64 + lane] = acc[rb][c][i];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      ring_barrier();
+      if (kh == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][c][i] += xch[((rb * 4 + c) * 4 + i) * 64 + lane];
+        store_nblock<MODE, RB>(p, acc, mem_ids, mb, nb0, lane);
+      }
+    } else if (!MULTI) {
+      store_nblock<MODE, RB>(p, acc, mem_ids, mb, nb0, lane);
+    }
   }
 }
 
@@ -310,17 +346,18 @@ int n_blocks_per_wave(const GemmParams& p) {
   return kn;
 }
 
-template <int MODE, int RB, int U, int DEPTH, bool MULTI>
+template <int MODE, int RB, int U, int DEPTH, bool MULTI, int KS>
 hipError_t launch_kn(const GemmParams& p, int kn, hipStream_t stream) {
-  using C = Cfg<RB, U, DEPTH>;
+  using C = Cfg<RB, U, DEPTH, KS>;
   constexpr int BM = 16 * RB;
-  const int64_t units_max = (int64_t)(p.capacity / BM) * (p.N / (kNBlock * kUnitNBlocks * kn));
+  const int64_t units_max = (int64_t)(p.capacity / BM) * (p.N / (kNBlock * (kUnitNBlocks / KS) * kn));
   if (units_max == 0) return hipSuccess;
   static int blocks_per_cu = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI, KS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI, KS>,
                                                      kThreads, C::kLdsBytes) != hipSuccess ||
         n < 1)
       n = 1;
@@ -331,16 +368,25 @@ hipError_t launch_kn(const GemmParams& p, int kn, hipStream_t stream) {
   // resident workgroup restarting its pipeline for a second unit (measured
   // faster for the decode down projection).
   const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu * 4);
-  hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI>), dim3((int)grid), dim3(kThreads),
+  hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI, KS>), dim3((int)grid), dim3(kThreads),
                      C::kLdsBytes, stream, p, kn);
   return hipGetLastError();
 }
 
+// Reductions of at least kSplitMinGroups groups at block_m 16 split each
+// n-block between two waves: the decode weight stream has too few units to
+// give every resident workgroup one (e.g. 40 active experts x 16 units against
+// 1024 resident slots), and twice the units keep more of it in flight.
+constexpr int kSplitMinGroups = 64;
+
 template <int MODE, int RB, int U, int DEPTH>
 hipError_t launch(const GemmParams& p, hipStream_t stream) {
   const int kn = n_blocks_per_wave(p);
-  return kn == 1 ? launch_kn<MODE, RB, U, DEPTH, false>(p, 1, stream)
-                 : launch_kn<MODE, RB, U, DEPTH, true>(p, kn, stream);
+  if (kn > 1) return launch_kn<MODE, RB, U, DEPTH, true, 1>(p, kn, stream);
+  if (RB == 1 && p.K / kGroup >= kSplitMinGroups && (p.K / kGroup) % (2 * U) == 0 &&
+      (p.N / kNBlock) % (kUnitNBlocks / 2) == 0)
+    return launch_kn<MODE, RB, U, DEPTH, false, 2>(p, 1, stream);
+  return launch_kn<MODE, RB, U, DEPTH, false, 1>(p, 1, stream);
 }
 
 template <int MODE>
