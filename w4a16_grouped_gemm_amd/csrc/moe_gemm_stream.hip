@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
 #pragma unroll
     for (int t = 0; t < C::kACopiesPerWave; ++t) {
       const int j = wave + 4 * t;
-      const int khj = j / (RB * U), jj = j % (RB * U);
+      const int khj = KS == 2 ? j / (RB * U) : 0, jj = KS == 2 ? j % (RB * U) : j;
       const int rb = jj / U, uu = jj % U;
       const int prow = mb * BM + rb * 16 + (lane & 15);
       const int id = p.sorted[prow];
@@ -245,6 +245,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
       for (int c = 0; c < 4; ++c) acc[rb][c] = zero4;
 
     u32x4 nib[DEPTH][U];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     ring_barrier();  // the previous unit's reads of every slot are done
     if (MULTI) {
       // Stores inside the weight stream read the row ids from LDS: a global
@@ -306,7 +307,9 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
     }
     if (KS == 2) {
       // the upper part's wave hands its partial sums to the lower part's wave
-      // through LDS (the rings are free once every wave passed this barrier)
+      // through LDS (the rings are free once every wave passed this barrier
+      // with its own ring reads complete)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       ring_barrier();
       float* xch = reinterpret_cast<float*>(lds) + (wave >> 1) * (RB * 16 * 64);
       if (kh == 1) {
