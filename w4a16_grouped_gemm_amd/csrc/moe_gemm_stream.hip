@@ -181,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = (int)threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < kThreads / 64);  // lets copy indices fold per unrolled step
   uint8_t* a_ring = lds;
   uint8_t* s_ring = lds + DEPTH * C::kABatchBytes + wave * DEPTH * C::kSBatchBytes;
   int* row_ids = reinterpret_cast<int*>(lds + DEPTH * C::kABatchBytes + 4 * DEPTH * C::kSBatchBytes);
