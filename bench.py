@@ -244,7 +244,8 @@ def main():
     ap.add_argument("--layout", default="routed", choices=["routed", "contiguous", "masked"],
                     help="routed: the layer on top-k routed ids (the default line); contiguous / masked: "
                          "the grouped-layout entry points")
-    ap.add_argument("--cpu-slots", type=int, default=64, help="resident slots the CPU baseline computes")
+    ap.add_argument("--cpu-slots", type=int, default=3000,
+                    help="resident slots the CPU baseline computes (all of them when the layer has fewer)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
