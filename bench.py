@@ -19,7 +19,7 @@ halves its read bandwidth.) Each step is timed with HIP events on the stream
 the kernels run on, with events between the stages for the per-kernel
 breakdown.
 
-Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus above 1 is refused: the layer here is one GPU's share and runs on one GPU.
 """
 from __future__ import annotations
 

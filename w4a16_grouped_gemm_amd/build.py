@@ -46,7 +46,7 @@ def build(verbose: bool = False) -> str:
     if msg.strip() and verbose:
         print(msg)
     # a shared library links with unresolved symbols; a missing kernel stub
-    # would only surface at load time on the GPU machine, so refuse it here
+    # would only surface at load time on the GPU, so refuse it here
     und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
     missing = [l.split()[-1] for l in und.splitlines() if "w4a16" in l]
     if missing:
