@@ -120,10 +120,11 @@ __device__ __forceinline__ void store_nblock(const GemmParams& p, floatx4 (&acc)
     for (int c = 0; c < 4; ++c) acc[rb][c] = zero4;
 }
 
-// KS: waves per n-block. KS = 2 splits each n-block's reduction between two
-// waves of the workgroup (groups [0, G/2) and [G/2, G)); a unit then covers 2
-// n-blocks, so a call has twice the units, and the two partial sums meet in
-// LDS at the end of the unit (added in that fixed order: deterministic).
+// KS: waves per n-block (1, 2 or 4). KS > 1 splits each n-block's reduction
+// between KS waves of the workgroup (wave part p reduces groups
+// [p G/KS, (p+1) G/KS)); a unit then covers 4/KS n-blocks, so a call has KS
+// times the units, and the partial sums meet in LDS at the end of the unit,
+// added in part order (deterministic).
 template <int RB, int U, int DEPTH, int KS = 1>
 struct Cfg {
   static constexpr int kABlocks = KS * RB * U;            // 1 KiB A fragments per batch (both halves)
@@ -175,7 +176,7 @@ __device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int a_slo
 // are copied during the first n-block only and stay resident for the others.
 template <int MODE, int RB, int U, int DEPTH, bool MULTI, int KS>
 __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p, int KN) {
-  static_assert(KS == 1 || (KS == 2 && !MULTI), "a split reduction runs one n-block per wave");
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && !MULTI), "a split reduction runs one n-block per wave");
   using C = Cfg<RB, U, DEPTH, KS>;
   constexpr int BM = 16 * RB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
   const int NG = NB / (kUnitNBlocks / KS * KN);  // units per row block
   const int G = p.K / kGroup;
   const int Gw = G / KS;                    // groups of one n-block this wave reduces
-  const int kh = KS == 2 ? (wave & 1) : 0;  // which part of K
+  const int kh = KS > 1 ? wave % KS : 0;    // which part of K
   const int nbatch = KN * Gw / U;           // batches per wave per unit
   const int kbatch = Gw / U;                // batches per n-block
   const bool a_resident = MULTI && kbatch <= DEPTH;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
 #pragma unroll
     for (int t = 0; t < C::kACopiesPerWave; ++t) {
       const int j = wave + 4 * t;
-      const int khj = KS == 2 ? j / (RB * U) : 0, jj = KS == 2 ? j % (RB * U) : j;
+      const int khj = KS > 1 ? j / (RB * U) : 0, jj = KS > 1 ? j % (RB * U) : j;
       const int rb = jj / U, uu = jj % U;
       const int prow = mb * BM + rb * 16 + (lane & 15);
       const int id = p.sorted[prow];
@@ -306,30 +307,33 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
         }
       }
     }
-    if (KS == 2) {
-      // the upper part's wave hands its partial sums to the lower part's wave
-      // through LDS (the rings are free once every wave passed this barrier
-      // with its own ring reads complete)
+    if (KS > 1) {
+      // the parts' waves hand their partial sums to part 0's wave through LDS
+      // (the rings are free once every wave passed this barrier with its own
+      // ring reads complete); part 0 adds them in part order
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       ring_barrier();
-      float* xch = reinterpret_cast<float*>(lds) + (wave >> 1) * (RB * 16 * 64);
-      if (kh == 1) {
+      constexpr int kPart = RB * 16 * 64;  // floats of one wave's accumulators
+      float* xch = reinterpret_cast<float*>(lds) + (wave / KS) * (KS - 1) * kPart;
+      if (kh > 0) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xch[((rb * 4 + c) * 4 + i) * 64 + lane] = acc[rb][c][i];
+            for (int i = 0; i < 4; ++i) xch[(kh - 1) * kPart + ((rb * 4 + c) * 4 + i) * 64 + lane] = acc[rb][c][i];
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       ring_barrier();
       if (kh == 0) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int q = 0; q < KS - 1; ++q)
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
+          for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rb][c][i] += xch[((rb * 4 + c) * 4 + i) * 64 + lane];
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[rb][c][i] += xch[q * kPart + ((rb * 4 + c) * 4 + i) * 64 + lane];
         store_nblock<MODE, RB>(p, acc, mem_ids, mb, nb0, lane);
       }
     } else if (!MULTI) {
