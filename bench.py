@@ -447,6 +447,9 @@ def main():
         "alg_flops": work["layer_flops"],
         "roofline": roof,
         "route_align_us": route_us,
+        "targets": {"decode_hbm_frac": 0.70, "prefill_mfma_frac": 0.50},
+        "context": "pages' per-layer speedups of NVIDIA kernels (Chord vs Humming): 1.11-1.33x on H200, "
+                   "1.81-2.15x on B300; context only, not a target on this GPU",
         "source_hash": kernel_source_hash(),
     }
     if args.copy_probe:
