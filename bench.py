@@ -293,6 +293,11 @@ def main():
     # and the light set at 16, each with its own h rows
     sets = [(128, split, 2**31 - 1), (16, 1, split - 1)] if split else [(bm, 0, 2**31 - 1)]
     bufs = [w.align_buffers(T, topk, E, b) for b, _, _ in sets]
+    if split:  # one sorted array for both sets, heavy part first (rounded to 64 ids), as in the one-call layer
+        hcap = -(-bufs[0]["sorted_token_ids"].numel() // 64) * 64
+        joined = torch.empty(hcap + bufs[1]["sorted_token_ids"].numel(), dtype=torch.int32, device="cuda")
+        bufs[0]["sorted_token_ids"], bufs[1]["sorted_token_ids"] = joined[:hcap], joined[hcap:]
+        bufs[0]["expert_ids"] = torch.empty(-(-hcap // 128), dtype=torch.int32, device="cuda")
     hs = [torch.empty((b["sorted_token_ids"].numel(), I), dtype=torch.int16, device="cuda") for b in bufs]
     y = torch.empty((T * topk, H), dtype=torch.float32, device="cuda")
     scratch = torch.empty(max(256, w.w4a16_moe_stage_workspace_bytes(shape, T, topk, sets[0][0])), dtype=torch.uint8,
@@ -309,9 +314,13 @@ def main():
         flush_buf.sum()
 
     def align():
-        for (b, lo, hi), buf in zip(sets, bufs):
-            w.moe_align_filtered(ids, E, b, lo, hi, buf["sorted_token_ids"], buf["expert_ids"],
-                                 buf["num_tokens_post_padded"], None, buf["workspace"])
+        if split:
+            w.moe_align_split(ids, E, split, 128, hcap, bufs[0]["expert_ids"], bufs[0]["num_tokens_post_padded"], 16,
+                              bufs[1]["expert_ids"], bufs[1]["num_tokens_post_padded"], joined, bufs[0]["workspace"])
+        else:
+            buf = bufs[0]
+            w.moe_align(ids, E, bm, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"], None,
+                        buf["workspace"])
 
     def gemm(stage, k):
         b, buf = sets[k][0], bufs[k]

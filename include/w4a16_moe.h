@@ -8,6 +8,9 @@
  * "런타임 고려사항"). The entry points, all on the caller's HIP stream:
  *
  *   moe_align           topk_ids -> sorted_token_ids, expert_ids, num_tokens_post_padded
+ *   moe_align_filtered / moe_align_split
+ *                       the same restricted to a band of per-expert counts; both
+ *                       bands of a heavy/light split in one pass
  *   moe_route_align     router logits -> top-k ids and weights, then moe_align
  *   w4a16_moe_forward   gate_up GEMM + SiLU-and-mul, down GEMM, top-k weighted combine
  *   w4a16_moe_routed_forward  alignment + the layer in one call, per-expert tile sizes
@@ -157,6 +160,29 @@ int moe_align_filtered(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t
                        int32_t min_count, int32_t max_count, int32_t* sorted_token_ids, int32_t capacity,
                        int32_t* expert_ids, int32_t* num_tokens_post_padded, int32_t* expert_counts,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Both halves of that split in one pass over the ids: the heavy set (experts
+ * with c >= split_count) at heavy_block_m and the light set (1 <= c <
+ * split_count) at light_block_m. The two sets share one sorted array:
+ * sorted_token_ids[0, heavy_capacity) is the heavy set's and
+ * sorted_token_ids[heavy_capacity, heavy_capacity + light_capacity) the light
+ * set's. Each set's sorted ids, expert ids and padded total are bit for bit
+ * those of moe_align_filtered with the matching range (expert counts are not
+ * written).
+ *   split_count      >= 2
+ *   heavy_capacity   >= moe_align_capacity(T, topk, E, heavy_block_m)
+ *   light_capacity   >= min(moe_align_capacity(T, topk, E, light_block_m),
+ *                           E * ceil((split_count - 1) / light_block_m) * light_block_m)
+ *   *_expert_ids     device int32 [ceil(*_capacity / *_block_m)]
+ *   workspace        as moe_align
+ * heavy_capacity + light_capacity must fit int32 (else W4A16_ERR_CAPACITY).
+ * W4A16_ERR_INVALID_ARG for split_count < 2 or a missing output; otherwise as
+ * moe_align. */
+int moe_align_split(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t split_count,
+                    int32_t heavy_block_m, int32_t heavy_capacity, int32_t* heavy_expert_ids,
+                    int32_t* heavy_num_tokens_post_padded, int32_t light_block_m, int32_t light_capacity,
+                    int32_t* light_expert_ids, int32_t* light_num_tokens_post_padded, int32_t* sorted_token_ids,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Router and alignment in one call: the step in front of the layer, with the
  * outputs of the FlashInfer Kimi-K3 fused router (page "[flashinfer]

@@ -148,6 +148,16 @@ def test_validation_status_codes(lib):
     assert lib.moe_align_filtered(FAKE, 4, 2, 8, 16, -1, 5, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 1
     assert lib.moe_align_filtered(FAKE, 4, 2, 8, 16, 6, 5, FAKE, 1000, FAKE, FAKE, None, None, 0, None) == 1
     assert lib.moe_align_filtered(FAKE, 4, 2, 8, 16, 1, 5, FAKE, 10, FAKE, FAKE, None, None, 0, None) == 3
+    # split alignment: T=4, topk=2, E=8; heavy needs 8 + 8*127 = 1024, light min(8 + 8*15, 8*32) = 128
+    def sp(split=32, hbm=128, hcap=1024, lbm=16, lcap=128, leids=FAKE):
+        return lib.moe_align_split(FAKE, 4, 2, 8, split, hbm, hcap, FAKE, FAKE, lbm, lcap, leids, FAKE, FAKE, None, 0,
+                                   None)
+    assert sp(split=1) == 1
+    assert sp(hbm=48) == 2 and sp(lbm=48) == 2              # unsupported block_m
+    assert sp(leids=None) == 1
+    assert sp(hcap=1023) == 3
+    assert sp(lcap=127) == 3
+    assert sp(hcap=2**31 - 100, lcap=200) == 3             # joined array beyond int32
     kimi = w.make_shape(48, 7168, 2048)
     assert w.w4a16_moe_routed_split(kimi, 16384, 8, 384) == 32     # prefill: heavy experts from 32 slots
     assert w.w4a16_moe_routed_split(kimi, 128, 8, 384) == 0        # decode: one alignment

@@ -56,6 +56,42 @@ def test_align_filtered(T, topk, E, bm, lo, hi, seed):
     np.testing.assert_array_equal(eids.cpu().numpy(), oe)
 
 
+@pytest.mark.parametrize("T,topk,E,split,hbm,lbm,seed", [
+    (300, 4, 16, 32, 128, 16, 1),        # one block per set
+    (5000, 8, 48, 32, 128, 16, 2),       # several chunks: the joined scatter
+    (5000, 8, 48, 2, 64, 32, 3),         # light set = experts with exactly one slot
+    (3000, 4, 16, 100000, 128, 16, 4),   # every resident expert light, heavy set empty
+    (0, 4, 16, 32, 128, 16, 5),          # no tokens
+])
+def test_align_split(T, topk, E, split, hbm, lbm, seed):
+    """Both sets of the one-pass split equal the oracle's alignments of the count-filtered ids."""
+    rng = np.random.default_rng(seed)
+    p = rng.zipf(1.3, size=E * 4).astype(np.float64)[:E + 4]
+    ids = (np.stack([rng.choice(E + 4, size=topk, replace=False, p=p / p.sum()) for _ in range(T)])
+           if T else np.zeros((0, topk))).astype(np.int32)
+    say(f"align split T={T} topk={topk} E={E} split={split} block_m {hbm}/{lbm}")
+    hcap = w.moe_align_capacity(T, topk, E, hbm) + 5          # not a multiple of anything
+    per = -(-(split - 1) // lbm) * lbm
+    lcap = min(w.moe_align_capacity(T, topk, E, lbm), E * per)
+    s = torch.full((hcap + lcap,), -7, dtype=torch.int32, device="cuda")
+    he = torch.full((-(-hcap // hbm),), -7, dtype=torch.int32, device="cuda")
+    le = torch.full((-(-lcap // lbm),), -7, dtype=torch.int32, device="cuda")
+    hn = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    ln = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    wsb = w.moe_align_workspace_bytes(T, topk, E, hbm)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda") if wsb else None
+    dev_ids = to_dev(ids) if T else torch.zeros((0, topk), dtype=torch.int32, device="cuda")
+    w.moe_align_split(dev_ids, E, split, hbm, hcap, he, hn, lbm, le, ln, s, ws)
+    torch.cuda.synchronize()
+    got = s.cpu().numpy()
+    for what, lo, hi, bm, cap, sl, e_, n_ in [("heavy", split, 2**31 - 1, hbm, hcap, slice(0, hcap), he, hn),
+                                             ("light", 1, split - 1, lbm, lcap, slice(hcap, hcap + lcap), le, ln)]:
+        os_, oe, on, _ = oracle.moe_align(filtered_ids(ids, E, lo, hi), E, bm, capacity=cap)
+        assert int(n_.item()) == on, what
+        np.testing.assert_array_equal(got[sl], os_, err_msg=what)
+        np.testing.assert_array_equal(e_.cpu().numpy(), oe, err_msg=what)
+
+
 def routed(d, Eg, x=None):
     c = d.case
     ws = torch.empty(w.w4a16_moe_routed_workspace_bytes(d.shape, c.T, c.topk, Eg), dtype=torch.uint8, device="cuda")
@@ -65,21 +101,25 @@ def routed(d, Eg, x=None):
     return out.cpu().numpy().view(np.uint16)
 
 
-def test_routed_small_skewed():
-    """An 8-expert slice of 16 routed experts, 64 routed tokens per expert -> block_m 128 and a
-    split: Zipf popularity leaves some local experts heavy and some light."""
-    c = synthetic.random_case("routed_small", T=512, H=256, I=128, E=8, topk=2, block_m=128, seed=33, E_global=16,
-                              logit_bias=synthetic.zipf_bias(16, s=1.5))
+@pytest.mark.parametrize("T,topk,E,Eg,s", [
+    (512, 2, 8, 16, 1.5),     # 1024 routed ids: one alignment block per set
+    (4096, 4, 16, 64, 1.1),   # 16384 routed ids: several chunks, one joined scatter for both sets
+])
+def test_routed_small_skewed(T, topk, E, Eg, s):
+    """An expert slice with block_m 128 by the tokens-per-expert rule and a split: Zipf
+    popularity leaves some local experts heavy and some light."""
+    c = synthetic.random_case("routed_small", T=T, H=256, I=128, E=E, topk=topk, block_m=128, seed=33, E_global=Eg,
+                              logit_bias=synthetic.zipf_bias(Eg, s=s))
     ids = c.topk_ids
     cnt = np.bincount(ids[ids < c.E], minlength=c.E)
     d = DeviceCase(c)
-    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, 16) == 32
+    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg) == 32
     assert (cnt >= 32).any() and ((cnt > 0) & (cnt < 32)).any(), cnt
-    say(f"routed small: counts {cnt.tolist()}")
-    out = routed(d, 16)
+    say(f"routed small T={T}: counts {cnt.tolist()}")
+    out = routed(d, Eg)
     ref = oracle.moe_layer(c.x, c.topk_ids, c.topk_weights, c.w13_q, c.w13_s, c.w2_q, c.w2_s, c.E, c.I)
-    parity(out, ref, "routed small skewed")
-    assert np.array_equal(out, routed(d, 16)), "run-to-run difference"
+    parity(out, ref, f"routed small skewed T={T}")
+    assert np.array_equal(out, routed(d, Eg)), "run-to-run difference"
 
 
 def test_routed_graph_replays():

@@ -14,7 +14,7 @@ from ._lib import LIB_PATH, Shape, load
 __all__ = [
     "W4A16Error", "Shape", "LIB_PATH", "load", "make_shape", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "moe_align_capacity", "moe_align_workspace_bytes", "w4a16_choose_block_m", "moe_align",
-    "moe_route_align", "moe_align_filtered", "w4a16_moe_routed_workspace_bytes", "w4a16_moe_routed_split",
+    "moe_route_align", "moe_align_filtered", "moe_align_split", "w4a16_moe_routed_workspace_bytes", "w4a16_moe_routed_split",
     "w4a16_moe_routed_forward", "w4a16_moe_contiguous_workspace_bytes", "w4a16_moe_contiguous_forward",
     "w4a16_moe_masked_block_m", "w4a16_moe_masked_workspace_bytes", "w4a16_moe_masked_forward",
     "w4a16_moe_stage_workspace_bytes", "w4a16_moe_prepare_x", "w4a16_moe_prepare_h",
@@ -132,6 +132,20 @@ def moe_align_filtered(topk_ids, num_experts: int, block_m: int, min_count: int,
                                      _p(sorted_token_ids), sorted_token_ids.numel(), _p(expert_ids),
                                      _p(num_tokens_post_padded), _p(expert_counts), _p(workspace), _nbytes(workspace),
                                      _stream(stream)), "moe_align_filtered")
+
+
+def moe_align_split(topk_ids, num_experts: int, split_count: int, heavy_block_m: int, heavy_capacity: int,
+                    heavy_expert_ids, heavy_num_tokens_post_padded, light_block_m: int, light_expert_ids,
+                    light_num_tokens_post_padded, sorted_token_ids, workspace=None, stream=None):
+    """Heavy and light alignments in one pass; sorted_token_ids holds the heavy set's
+    heavy_capacity ids, then the light set's (the rest of the tensor)."""
+    T, topk = topk_ids.shape
+    light_capacity = sorted_token_ids.numel() - heavy_capacity
+    _check(load().moe_align_split(_p(topk_ids), T, topk, num_experts, split_count, heavy_block_m, heavy_capacity,
+                                  _p(heavy_expert_ids), _p(heavy_num_tokens_post_padded), light_block_m,
+                                  light_capacity, _p(light_expert_ids), _p(light_num_tokens_post_padded),
+                                  _p(sorted_token_ids), _p(workspace), _nbytes(workspace), _stream(stream)),
+           "moe_align_split")
 
 
 def w4a16_moe_routed_workspace_bytes(shape: Shape, T: int, topk: int, num_experts_global: int) -> int:

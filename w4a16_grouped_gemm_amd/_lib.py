@@ -27,6 +27,7 @@ SIGNATURES = {
     "w4a16_choose_block_m": (I32, [I32, I32, I32, I32]),
     "moe_align": (ctypes.c_int, [P, I32, I32, I32, I32, P, I32, P, P, P, P, SZ, P]),
     "moe_align_filtered": (ctypes.c_int, [P, I32, I32, I32, I32, I32, I32, P, I32, P, P, P, P, SZ, P]),
+    "moe_align_split": (ctypes.c_int, [P, I32, I32, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P, SZ, P]),
     "w4a16_moe_routed_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_routed_split": (I32, [P, I32, I32, I32]),
     "w4a16_moe_routed_forward": (ctypes.c_int, [P, P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),

@@ -112,8 +112,9 @@ __device__ __forceinline__ void count_ids(const int (&v)[kPerThread], int E, int
 // padded total), cursor[e] = off[e] (+ the old cursor[e] when add_cursor), and,
 // where the pointers are not null, the counts and the padded total to global
 // memory. An expert whose count lies outside `keep` is dropped: its count
-// becomes 0 (in LDS too, which the scatter reads) and its ids are skipped. Lane l owns experts [l * per, (l + 1) * per), held in registers; one
-// DPP wave scan. E <= 64 * kMaxExpertsPerLane.
+// becomes 0 (in LDS too, which the scatter reads) and its ids are skipped.
+// Lane l owns experts [l * per, (l + 1) * per), held in registers; one DPP
+// wave scan. E <= 64 * kMaxExpertsPerLane.
 constexpr int kMaxExpertsPerLane = 8;
 
 // Experts kept by an alignment: those with lo <= count <= hi.
@@ -394,6 +395,67 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
   scatter_ids(v, steps, E, id_bits(E), counts, cursor, wtab, sorted, capacity, lo);
 }
 
+// Two alignments of the same ids in one pass: experts with at least `split`
+// resident ids form set 0 (block_m bm0), those with 1 .. split - 1 set 1
+// (block_m bm1); each set's outputs are exactly the one-set alignment with
+// that count range. Set 1's sorted array directly follows set 0's (sorted +
+// cap0), so one stable scatter into the joined array serves both: an expert of
+// set 1 starts its cursor at cap0 + its offset in set 1.
+// LDS: cnt0[E], off0[E+1], cur0[E], wtab[kWaves*E], cnt1[E], off1[E+1],
+// cur1[E], kept[E]
+__global__ __launch_bounds__(kThreads) void align_scatter2_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                                  int split, const int* __restrict__ hist, int nchunks,
+                                                                  int32_t* __restrict__ sorted, int bm0, int cap0,
+                                                                  int32_t* __restrict__ eids0, int nblk0,
+                                                                  int32_t* __restrict__ ntpp0, int bm1, int cap1,
+                                                                  int32_t* __restrict__ eids1, int nblk1,
+                                                                  int32_t* __restrict__ ntpp1) {
+  extern __shared__ int smem[];
+  int* cnt0 = smem;
+  int* off0 = cnt0 + E;
+  int* cur0 = off0 + E + 1;
+  int* wtab = cur0 + E;
+  int* cnt1 = wtab + kWaves * E;
+  int* off1 = cnt1 + E;
+  int* cur1 = off1 + E + 1;
+  int* kept = cur1 + E;
+  int v[kPerThread];
+  const int lo = (int)blockIdx.x * kChunk;
+  const int steps = block_steps(lo, min(n, lo + kChunk));
+  load_ids(ids, lo, min(n, lo + kChunk), steps, v);
+  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
+  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
+    int total = 0, before = 0;
+#pragma unroll 8
+    for (int b = 0; b < nchunks; ++b) {
+      const int c = hist[(size_t)b * E + e];
+      before += (b < (int)blockIdx.x) ? c : 0;
+      total += c;
+    }
+    cnt0[e] = cnt1[e] = total;
+    cur0[e] = cur1[e] = before;
+  }
+  lds_barrier();
+  const bool first = blockIdx.x == 0;
+  // both scans run on wave 0, one after the other (its LDS accesses stay in order)
+  scan_offsets(cnt0, E, bm0, off0, cur0, true, nullptr, first ? ntpp0 : nullptr, CountRange{split, 0x7fffffff});
+  scan_offsets(cnt1, E, bm1, off1, cur1, true, nullptr, first ? ntpp1 : nullptr, CountRange{1, split - 1});
+  lds_barrier();
+  const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
+  label_blocks(off0, cnt0, E, bm0, sorted, eids0, nblk0, cap0, n, gt >> 4, gstep / 16);
+  label_blocks(off1, cnt1, E, bm1, sorted + cap0, eids1, nblk1, cap1, n, gt >> 4, gstep / 16);
+  fill_tail(off0[E], bm0, sorted, cap0, eids0, nblk0, n, gt, gstep);
+  fill_tail(off1[E], bm1, sorted + cap0, cap1, eids1, nblk1, n, gt, gstep);
+  // joined view: kept[e] = the expert's count in whichever set holds it (the
+  // ranges are disjoint), cur1[e] = its cursor in the joined array
+  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
+    kept[e] = cnt0[e] + cnt1[e];
+    cur1[e] = cnt0[e] > 0 ? cur0[e] : cap0 + cur1[e];
+  }
+  lds_barrier();
+  scatter_ids(v, steps, E, id_bits(E), kept, cur1, wtab, sorted, cap0 + cap1, lo);
+}
+
 // T == 0: every output is a sentinel.
 __global__ void align_empty_kernel(int32_t* sorted, int capacity, int sentinel, int32_t* expert_ids, int nblk,
                                    int32_t* ntpp_out, int32_t* counts_out, int E) {
@@ -585,6 +647,8 @@ __global__ __launch_bounds__(kThreads) void route_align_small_kernel(
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t scatter_lds(int E) { return sizeof(int) * (size_t)(3 * E + 1 + kWaves * E); }
+// align_scatter2_kernel: the one-set layout, then cnt1[E], off1[E+1], cur1[E], kept[E]
+size_t scatter2_lds(int E) { return scatter_lds(E) + sizeof(int) * (size_t)(4 * E + 1); }
 
 }  // namespace
 
@@ -596,7 +660,7 @@ size_t align_workspace_bytes(int64_t n, int32_t E) {
 
 hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, int32_t* sorted, int32_t capacity,
                         int32_t* expert_ids, int32_t* ntpp, int32_t* counts, void* workspace, hipStream_t stream,
-                        int32_t min_count, int32_t max_count, bool reuse_hist) {
+                        int32_t min_count, int32_t max_count) {
   const int nblk = (capacity + bm - 1) / bm;
   const CountRange keep = {min_count, max_count};
   if (n == 0) {
@@ -612,14 +676,33 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, in
   }
   const int nchunks = (n + kChunk - 1) / kChunk;
   int* hist = static_cast<int*>(workspace);
-  if (!reuse_hist) {
-    hipLaunchKernelGGL(align_hist_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, stream, ids, n, E,
-                       hist);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, stream, ids, n, E,
+                     hist);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, hist,
                      nchunks, sorted, capacity, expert_ids, nblk, ntpp, counts, keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_align_split(const int32_t* ids, int32_t n, int32_t E, int32_t split, int32_t* sorted, int32_t bm0,
+                              int32_t cap0, int32_t* eids0, int32_t* ntpp0, int32_t bm1, int32_t cap1,
+                              int32_t* eids1, int32_t* ntpp1, void* workspace, hipStream_t stream) {
+  if (n <= kSmallMax) {  // one block per set already: the two one-set alignments
+    const hipError_t err = launch_align(ids, n, E, bm0, sorted, cap0, eids0, ntpp0, nullptr, workspace, stream,
+                                        split, 0x7fffffff);
+    if (err != hipSuccess) return err;
+    return launch_align(ids, n, E, bm1, sorted + cap0, cap1, eids1, ntpp1, nullptr, workspace, stream, 1, split - 1);
+  }
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  int* hist = static_cast<int*>(workspace);
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, stream, ids, n, E,
+                     hist);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(align_scatter2_kernel, dim3(nchunks), dim3(kThreads), scatter2_lds(E), stream, ids, n, E, split,
+                     hist, nchunks, sorted, bm0, cap0, eids0, (cap0 + bm0 - 1) / bm0, ntpp0, bm1, cap1, eids1,
+                     (cap1 + bm1 - 1) / bm1, ntpp1);
   return hipGetLastError();
 }
 

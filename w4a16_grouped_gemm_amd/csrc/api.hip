@@ -16,6 +16,13 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Capacity the light set of a split alignment needs: every light expert holds
+// at most split - 1 ids, so at most that many rounded up to block_m once padded.
+size_t split_light_capacity(int32_t T, int32_t topk, int32_t E, int32_t split, int32_t bm) {
+  const size_t per = ((size_t)(split - 1) + bm - 1) / bm * bm;
+  return std::min<size_t>((size_t)T * topk + (size_t)E * (bm - 1), (size_t)E * per);
+}
+
 bool block_m_ok(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
 int check_shape(const w4a16_moe_shape* s) {
@@ -154,6 +161,32 @@ int moe_align_filtered(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t
   return hip_status(launch_align(topk_ids, T * topk, num_experts, block_m, sorted_token_ids, capacity, expert_ids,
                                  num_tokens_post_padded, expert_counts, workspace, static_cast<hipStream_t>(stream),
                                  min_count, max_count));
+}
+
+int moe_align_split(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t num_experts, int32_t split_count,
+                    int32_t heavy_block_m, int32_t heavy_capacity, int32_t* heavy_expert_ids,
+                    int32_t* heavy_num_tokens_post_padded, int32_t light_block_m, int32_t light_capacity,
+                    int32_t* light_expert_ids, int32_t* light_num_tokens_post_padded, int32_t* sorted_token_ids,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_tokens(T, topk, num_experts, heavy_block_m);
+  if (st != W4A16_OK) return st;
+  if ((st = check_tokens(T, topk, num_experts, light_block_m)) != W4A16_OK) return st;
+  if (split_count < 2) return W4A16_ERR_INVALID_ARG;
+  if ((T > 0 && !topk_ids) || !sorted_token_ids || !heavy_expert_ids || !heavy_num_tokens_post_padded ||
+      !light_expert_ids || !light_num_tokens_post_padded)
+    return W4A16_ERR_INVALID_ARG;
+  if (heavy_capacity < 0 || (size_t)heavy_capacity < moe_align_capacity(T, topk, num_experts, heavy_block_m))
+    return W4A16_ERR_CAPACITY;
+  if (light_capacity < 0 || (size_t)light_capacity < split_light_capacity(T, topk, num_experts, split_count,
+                                                                          light_block_m))
+    return W4A16_ERR_CAPACITY;
+  if ((int64_t)heavy_capacity + light_capacity > INT32_MAX) return W4A16_ERR_CAPACITY;
+  const size_t ws = align_workspace_bytes((int64_t)T * topk, num_experts);
+  if (ws > 0 && (!workspace || workspace_bytes < ws)) return W4A16_ERR_WORKSPACE;
+  return hip_status(launch_align_split(topk_ids, T * topk, num_experts, split_count, sorted_token_ids, heavy_block_m,
+                                       heavy_capacity, heavy_expert_ids, heavy_num_tokens_post_padded, light_block_m,
+                                       light_capacity, light_expert_ids, light_num_tokens_post_padded, workspace,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 int moe_route_align(const float* logits, const float* bias, int32_t T, int32_t num_routed_experts, int32_t topk,
@@ -485,6 +518,7 @@ constexpr int32_t kHeavyBlockM = 128;
 struct AlignSet {
   size_t sorted, expert_ids, ntpp, h;
   int32_t block_m, capacity;
+  int32_t gemm_rows;  // rows the set's GEMMs cover: the live rows fit in them (ntpp <= gemm_rows <= capacity)
 };
 
 struct RoutedWorkspace {
@@ -504,13 +538,27 @@ RoutedWorkspace routed_workspace(const w4a16_moe_shape* s, int32_t T, int32_t to
   size_t off = 0;
   r.hist = off;
   off += round_up(align_workspace_bytes((int64_t)T * topk, E));
+  r.set[0].capacity = (int32_t)moe_align_capacity(T, topk, E, r.set[0].block_m);
+  // the tiled stages place their prepared rows and row exponents by this row
+  // count, so it stays the one the stage workspace is sized for
+  r.set[0].gemm_rows = r.set[0].capacity;
+  if (r.split) {
+    // one joined scatter fills both sets: the light set's sorted array follows
+    // the heavy set's, whose capacity is rounded up to 64 ids so the light
+    // array keeps the 256-byte alignment of the other buffers
+    r.set[0].capacity = (r.set[0].capacity + 63) / 64 * 64;
+    r.set[1].capacity = (int32_t)split_light_capacity(T, topk, E, kHeavyRows, kLightBlockM);
+    r.set[1].gemm_rows = r.set[1].capacity;
+  }
+  r.set[0].sorted = off;
+  off += (size_t)r.set[0].capacity * 4;
+  if (r.split) {
+    r.set[1].sorted = off;
+    off += (size_t)r.set[1].capacity * 4;
+  }
+  off = round_up(off);
   for (int k = 0; k < nsets; ++k) {
     AlignSet& a = r.set[k];
-    a.capacity = (int32_t)moe_align_capacity(T, topk, E, a.block_m);
-    // a light expert holds fewer than kHeavyRows slots: at most kHeavyRows rows once padded
-    if (k == 1) a.capacity = std::min<int32_t>(a.capacity, E * kHeavyRows);
-    a.sorted = off;
-    off += round_up((size_t)a.capacity * 4);
     a.expert_ids = off;
     off += round_up(((size_t)a.capacity + a.block_m - 1) / a.block_m * 4);
     a.ntpp = off;
@@ -574,21 +622,21 @@ int w4a16_moe_routed_forward(const w4a16_moe_shape* shape, const uint16_t* x, in
   float* y = reinterpret_cast<float*>(ws + r.y);
   void* scratch = ws + r.scratch;
   void* hist = ws + r.hist;
-  // alignments: the heavy set (or the only one), then the light set over the same histograms
-  for (int k = 0; k < nsets; ++k) {
-    const int32_t lo = !r.split ? 0 : (k == 0 ? kHeavyRows : 1);
-    const int32_t hi = !r.split ? INT32_MAX : (k == 0 ? INT32_MAX : kHeavyRows - 1);
-    st = hip_status(launch_align(topk_ids, T * topk, E, r.set[k].block_m, sorted[k], r.set[k].capacity, eids[k],
-                                 ntpp[k], nullptr, hist, hs, lo, hi, k > 0));
-    if (st != W4A16_OK) return st;
-  }
+  if (r.split)  // both sets in one pass over the ids
+    st = hip_status(launch_align_split(topk_ids, T * topk, E, kHeavyRows, sorted[0], r.set[0].block_m,
+                                       r.set[0].capacity, eids[0], ntpp[0], r.set[1].block_m, r.set[1].capacity,
+                                       eids[1], ntpp[1], hist, hs));
+  else
+    st = hip_status(launch_align(topk_ids, T * topk, E, r.set[0].block_m, sorted[0], r.set[0].capacity, eids[0],
+                                 ntpp[0], nullptr, hist, hs));
+  if (st != W4A16_OK) return st;
   st = w4a16_moe_prepare_x(shape, x, T, topk, topk_ids, r.set[0].block_m, scratch, r.scratch_bytes, stream);
   if (st != W4A16_OK) return st;
   const int32_t H = shape->hidden, I = shape->intermediate;
   // the light set's capacity is below moe_align_capacity, so its GEMMs are launched here directly
   const auto gemm = [&](GemmMode mode, int k) {
     const bool up = mode == kGateUp;
-    GemmParams p = gemm_params(shape, T, topk, sorted[k], r.set[k].capacity, eids[k], ntpp[k],
+    GemmParams p = gemm_params(shape, T, topk, sorted[k], r.set[k].gemm_rows, eids[k], ntpp[k],
                                up ? w13_packed : w2_packed, up ? 2 * I : H, up ? H : I);
     p.a = up ? x : h[k];
     p.out = up ? static_cast<void*>(h[k]) : static_cast<void*>(y);
@@ -597,7 +645,7 @@ int w4a16_moe_routed_forward(const w4a16_moe_shape* shape, const uint16_t* x, in
   };
   for (int k = 0; k < nsets; ++k)
     if ((st = gemm(kGateUp, k)) != W4A16_OK) return st;
-  st = w4a16_moe_prepare_h(shape, T, topk, h[0], sorted[0], r.set[0].capacity, ntpp[0], r.set[0].block_m, scratch,
+  st = w4a16_moe_prepare_h(shape, T, topk, h[0], sorted[0], r.set[0].gemm_rows, ntpp[0], r.set[0].block_m, scratch,
                            r.scratch_bytes, stream);
   if (st != W4A16_OK) return st;
   for (int k = 0; k < nsets; ++k)

@@ -85,13 +85,17 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 
 // Launchers: return hipSuccess or the launch error. All run on `stream`.
 // Alignment of n routed ids over experts [0, E). Experts whose resident count
-// lies outside [min_count, max_count] are treated as not resident. With
-// reuse_hist, the per-chunk histograms already in `workspace` (from a launch
-// over the same ids) are used as they are (inputs above one chunk only).
+// lies outside [min_count, max_count] are treated as not resident.
 hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t block_m, int32_t* sorted,
                         int32_t capacity, int32_t* expert_ids, int32_t* ntpp, int32_t* counts,
                         void* workspace, hipStream_t stream, int32_t min_count = 0,
-                        int32_t max_count = 0x7fffffff, bool reuse_hist = false);
+                        int32_t max_count = 0x7fffffff);
+// Two count-range alignments of the same ids: [split, max] at block_m bm0 into
+// sorted[0, cap0), and [1, split - 1] at bm1 into sorted[cap0, cap0 + cap1);
+// each equals launch_align with that range. Same workspace as launch_align.
+hipError_t launch_align_split(const int32_t* ids, int32_t n, int32_t E, int32_t split, int32_t* sorted, int32_t bm0,
+                              int32_t cap0, int32_t* eids0, int32_t* ntpp0, int32_t bm1, int32_t cap1,
+                              int32_t* eids1, int32_t* ntpp1, void* workspace, hipStream_t stream);
 size_t align_workspace_bytes(int64_t n, int32_t E);
 
 // Top-k routing of fp32 logits [T, Eg] (+ optional bias [Eg]) into topk_ids /
