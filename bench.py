@@ -236,7 +236,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the MFMA-bound prefill layers run ~20% slow for ~15 ms after the GPU comes out of idle (clock and
+    # power settling, seen in kernel traces); 30 untimed steps cover that, a few ms of GPU time
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--block-m", type=int, default=0, help="0: the tokens-per-expert heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -39,6 +39,9 @@ SMALL = [
     ("bm128 mixed paths", 200, 320, 128, 4, 2, 4, 128),   # gate_up tiled, down streamed (H % 256 != 0)
     ("bm128 streamed", 200, 512, 96, 4, 2, 4, 128),       # neither GEMM fits the tiled kernel
     ("many experts", 96, 256, 64, 200, 8, 256, 16),
+    # the declared maxima: 512 resident experts, top-32 routing
+    ("max experts, max topk", 40, 256, 64, 512, 32, 512, 16),
+    ("max topk bm128", 48, 384, 128, 40, 32, 40, 128),
     # short reductions: the down projection's waves run through several n-blocks
     ("short K bm16", 64, 1024, 256, 8, 2, 8, 16),
     ("short K bm32", 64, 1024, 256, 8, 2, 8, 32),
