@@ -28,6 +28,9 @@
 // Small inputs run in one block and one launch. Larger ones use two launches:
 // per-chunk histograms, then one block per chunk that recomputes the (small)
 // expert prefix itself from all chunk histograms and scatters its chunk.
+// A heavy/light split by per-expert count (two block sizes for skewed
+// routing) shares the histogram launch and one scatter launch: each block
+// scans both count bands and scatters into the two sets' joined sorted array.
 #include "internal.h"
 #include "w4a16_moe.h"
 
