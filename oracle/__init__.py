@@ -53,6 +53,8 @@ def _load():
         lib.oracle_route_topk.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -121,6 +123,11 @@ def round_bf16(v: float) -> float:
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the following layer calls use (the baseline's one-core timing)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def moe_layer(x_bits, topk_ids, topk_weights, w13_q, w13_s, w2_q, w2_s, E: int, I: int,

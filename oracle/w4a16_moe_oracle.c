@@ -263,3 +263,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads the next layer calls use (n >= 1; for timing the baseline on one core). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n < 1 ? 1 : n);
+#else
+  (void)n;
+#endif
+}
