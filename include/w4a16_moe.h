@@ -161,9 +161,10 @@ int moe_align_filtered(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t
                        int32_t* expert_ids, int32_t* num_tokens_post_padded, int32_t* expert_counts,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Both halves of that split in one pass over the ids: the heavy set (experts
- * with c >= split_count) at heavy_block_m and the light set (1 <= c <
- * split_count) at light_block_m. The two sets share one sorted array:
+/* Both halves of that split in one pass over the ids (per-expert tile sizes
+ * chosen by each expert's token count: Chord page, "인덱스 커널 기법"): the
+ * heavy set (experts with c >= split_count) at heavy_block_m and the light set
+ * (1 <= c < split_count) at light_block_m. The two sets share one sorted array:
  * sorted_token_ids[0, heavy_capacity) is the heavy set's and
  * sorted_token_ids[heavy_capacity, heavy_capacity + light_capacity) the light
  * set's. Each set's sorted ids, expert ids and padded total are bit for bit
