@@ -116,6 +116,31 @@ def dequant(q, s, N: int, K: int) -> np.ndarray:
     return w
 
 
+def expert_rows(a_bits, row_expert, w_q, w_s, N: int, K: int) -> np.ndarray:
+    """fp64 [R, N]: each activation row times its expert's weights, transposed.
+
+    Row r of a (bf16 bits [R, K]) against the exactly dequantised weights
+    (int4 times bf16 group scale) of expert row_expert[r] ([E, N, K/2] nibbles,
+    [E, N, K/32] scales); rows whose expert is negative give 0. This is one
+    projection of one local slot in the layer definition (g = x . W13^T before
+    SiLU-and-mul, y = h . W2^T before the weighted combine), for checking a
+    GEMM stage on the very rows it was given. The matmul is numpy's, in fp64.
+    """
+    a = _c(a_bits, np.uint16)
+    R = a.shape[0]
+    assert a.shape == (R, K)
+    af = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ex = np.asarray(row_expert, np.int64).reshape(R)
+    E = _c(w_q, np.uint8).size // (N * (K // 2))
+    q = _c(w_q, np.uint8).reshape(E, N, K // 2)
+    sc = _c(w_s, np.uint16).reshape(E, N, K // 32)
+    out = np.zeros((R, N), np.float64)
+    for e in np.unique(ex[ex >= 0]):
+        rows = np.nonzero(ex == e)[0]
+        out[rows] = af[rows] @ dequant(q[e], sc[e], N, K).astype(np.float64).T
+    return out
+
+
 def round_bf16(v: float) -> float:
     """The oracle's own double -> bf16 round-to-nearest-even."""
     return _load().oracle_round_bf16(float(v))

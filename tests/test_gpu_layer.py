@@ -144,6 +144,64 @@ def test_zero_tokens():
     assert d.forward(16, ids=ids, wts=wts, x=x).shape == (0, 256)
 
 
+# 48 experts x 128 rows (contiguous routing) with more 128 x 256 tiles than
+# resident workgroups, so every workgroup runs several tiles. Each GEMM stage
+# is checked on the very rows it was given (the exact projections of those
+# rows), so a wrong tile shows at once with a bound far tighter than the
+# layer's, whatever the bf16 rounding of h does elsewhere: with I = 128 the
+# layer output itself can exceed the layer bound on a few elements of a row
+# whose h has one element rounded the other way on the two sides.
+TILED_STAGES = [
+    ("gate_up many tiles", 128, 2048),   # gate_up: 768 tiles of 2 stages; down streamed (H < 256)
+    ("down many tiles", 7168, 128),      # down: 1344 tiles of 2 stages; gate_up 48 tiles of 112
+]
+
+
+@pytest.mark.parametrize("name,H,I", TILED_STAGES, ids=[s[0] for s in TILED_STAGES])
+def test_tiled_stages_on_own_rows(name, H, I):
+    c = synthetic.contiguous_case(seed=7, H=H, I=I)
+    bm, T, k = c.block_m, c.T, c.topk
+    say(f"layer {name}: T={T} H={H} I={I} E={c.E} bm={bm}")
+    d = DeviceCase(c)
+    buf = d.align(bm)
+    srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+    h = torch.zeros((srt.numel(), I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((T * k, H), dtype=torch.float32, device="cuda")
+    out = torch.full((T, H), -1, dtype=torch.int16, device="cuda")
+    ws = torch.empty(w.w4a16_moe_stage_workspace_bytes(d.shape, T, k, bm), dtype=torch.uint8, device="cuda")
+    w.w4a16_moe_prepare_x(d.shape, d.x, d.ids, bm, ws)
+    w.w4a16_moe_gate_up(d.shape, d.x, T, k, srt, eid, ntpp, bm, d.w13p, h, ws)
+    w.w4a16_moe_prepare_h(d.shape, T, k, h, srt, ntpp, bm, ws)
+    w.w4a16_moe_down(d.shape, T, k, h, srt, eid, ntpp, bm, d.w2p, y, ws)
+    w.w4a16_moe_combine(d.shape, d.ids, d.wts, y, out)
+    torch.cuda.synchronize()
+    n = int(ntpp.item())
+    rows = np.arange(n)
+    slot = srt.cpu().numpy()[:n]
+    real = slot < T * k
+    rows, slot = rows[real], slot[real]
+    ex = eid.cpu().numpy()[rows // bm]
+    # gate_up: h = bf16(silu(g) * u) with g, u the exact fp64 projections of the row's token
+    g = oracle.expert_rows(c.x[slot // k], ex, c.w13_q, c.w13_s, 2 * I, H)
+    h_exact = g[:, :I] / (1.0 + np.exp(-g[:, :I])) * g[:, I:]
+    h_gpu = bf16_to_f64(h.cpu().numpy()[rows])
+    err = np.abs(h_gpu - h_exact)
+    tol = 2.0**-6 * np.abs(h_exact) + 1e-4
+    say(f"  gate_up rows: max err/tol {float((err / tol).max()):.4f}")
+    assert np.all(err <= tol), f"{name}: gate_up rows off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
+    # down: y = h . W2^T of the GPU's own h rows, in fp32 against fp64
+    y_ref = oracle.expert_rows(h.cpu().numpy()[rows].view(np.uint16), ex, c.w2_q, c.w2_s, H, I)
+    y_gpu = y.cpu().numpy()[slot].astype(np.float64)
+    err = np.abs(y_gpu - y_ref)
+    tol = 1e-4 * (np.abs(y_ref) + np.abs(y_ref).max(axis=1, keepdims=True))
+    say(f"  down rows: max err/tol {float((err / tol).max()):.4f}")
+    assert np.all(err <= tol), f"{name}: down rows off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
+    # the one-call layer gives the same bits, run after run
+    one = d.forward(bm)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), one)
+    assert np.array_equal(one, d.forward(bm)), "run-to-run difference"
+
+
 FULL = ["decode_ep48", "islice_tp8", "prefill_contig48", "prefill_skew48"]
 
 

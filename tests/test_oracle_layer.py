@@ -252,3 +252,60 @@ def test_one_hot_routing_is_single_expert_ffn(oracle_lib):
         g = w13 @ xf[t]
         h = _bf16(g[:c.I] / (1 + np.exp(-g[:c.I])) * g[c.I:])
         np.testing.assert_allclose(out[t], w2 @ h, rtol=1e-9, atol=1e-9)
+
+
+def test_expert_rows_brute_force_and_one_hot(oracle_lib):
+    """expert_rows against pure-Python loops with their own nibble decode, and
+    one-hot rows that pick out one dequantised weight column exactly."""
+    import oracle
+
+    rng = np.random.default_rng(11)
+    E, N, K, R = 3, 5, 64, 7
+    qv = rng.integers(-8, 8, size=(E, N, K))
+    codes = (qv & 0xF).astype(np.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    s_bits = synthetic.to_bf16_bits(rng.uniform(0.005, 0.02, size=(E, N, K // 32)).astype(np.float32))
+    x_bits = synthetic.to_bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    ex = np.array([0, 2, -1, 1, 2, 0, 1])
+    got = oracle.expert_rows(x_bits, ex, packed, s_bits, N, K)
+
+    def f(bits):
+        return float(np.array([int(bits) << 16], np.uint32).view(np.float32)[0])
+
+    for r in range(R):
+        for n in range(N):
+            ref = 0.0
+            if ex[r] >= 0:
+                for k in range(K):
+                    byte = int(packed[ex[r], n, k // 2])
+                    nib = (byte >> 4) if k % 2 else (byte & 0xF)
+                    qi = nib - 16 if nib >= 8 else nib
+                    ref += f(x_bits[r, k]) * qi * f(s_bits[ex[r], n, k // 32])
+            assert abs(got[r, n] - ref) <= 1e-12 * max(1.0, abs(ref)), (r, n)
+    # one-hot rows: the weight q * s of column k, exactly
+    one = np.zeros((K, K), np.float32)
+    one[np.arange(K), np.arange(K)] = 1.0
+    cols = oracle.expert_rows(synthetic.to_bf16_bits(one), np.full(K, 1), packed, s_bits, N, K)
+    want = qv[1].T * np.repeat(brute.bf16_bits_to_f64(s_bits[1]), 32, axis=1).T
+    assert np.array_equal(cols, want)
+
+
+def test_expert_rows_recompose_layer(oracle_lib):
+    """The layer rebuilt from expert_rows (gate_up rows, bf16 SiLU-and-mul, down
+    rows, weighted sum in slot order) equals the layer oracle."""
+    import oracle
+
+    c = _small()
+    T, k = c.topk_ids.shape
+    ids = c.topk_ids.reshape(-1)
+    local = (ids >= 0) & (ids < c.E)
+    ex = np.where(local, ids, -1)
+    xr = np.repeat(c.x, k, axis=0)
+    g = oracle.expert_rows(xr, ex, c.w13_q, c.w13_s, 2 * c.I, c.H)
+    a = g[:, :c.I] / (1.0 + np.exp(-g[:, :c.I])) * g[:, c.I:]
+    h = synthetic.to_bf16_bits(_bf16(a).astype(np.float32))
+    y = oracle.expert_rows(h, ex, c.w2_q, c.w2_s, c.H, c.I)
+    out = np.zeros((T, c.H))
+    for j in range(k):
+        out += np.where(local.reshape(T, k)[:, j:j + 1], c.topk_weights[:, j:j + 1] * y.reshape(T, k, -1)[:, j], 0.0)
+    np.testing.assert_allclose(out, _run(oracle_lib, c), rtol=1e-9, atol=1e-9)
