@@ -59,10 +59,11 @@ def decode_packed(buf: np.ndarray, E: int, N: int, K: int, gate_up_I: int):
 
 
 def expected_f16(s_bits: np.ndarray):
-    """Channel exponents and normalised fp16 scales of bf16 scale bits [E, N, G]."""
+    """Channel exponents (the largest |s|'s exponent minus 4) and normalised fp16
+    scales (largest in [16, 32)) of bf16 scale bits [E, N, G]."""
     mx = (s_bits & 0x7FFF).max(axis=-1).astype(np.int32)
     ef = mx >> 7
-    ex = np.where(mx == 0, 0, np.where(ef == 0, -126, ef - 127)).astype(np.int32)
+    ex = (np.where(mx == 0, 0, np.where(ef == 0, -126, ef - 127)) - 4).astype(np.int32)
     v = np.ldexp((s_bits.astype(np.uint32) << 16).view(np.float32), -ex[..., None]).astype(np.float32)
     return ex, v.astype(np.float16)
 

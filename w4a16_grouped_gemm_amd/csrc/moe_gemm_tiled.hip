@@ -11,10 +11,11 @@
 // Arithmetic: fp16 operands on v_mfma_f32_16x16x32_f16, fp32 accumulation.
 // Both operands are exact images of the bf16/int4 inputs:
 //   * weights: q * s' where s' = s * 2^-E_n is the group scale normalised by a
-//     power of two per output channel (E_n from the channel's largest scale).
-//     q has at most 4 significant bits and s' at most 8, so q * s' is an exact
-//     fp16 value; it is formed with two exact packed-fp16 operations from the
-//     code (q + 8) OR-ed into the mantissa of fp16 1024.0.
+//     power of two per output channel (the channel's largest scale lands in
+//     [16, 32)). q has at most 3 significant bits and s' at most 8, so q * s'
+//     is an exact fp16 value; it is formed with two exact packed-fp16
+//     operations from the code (q + 8) OR-ed into the mantissa of fp16 1024.0
+//     (see dequant).
 //   * activations: rows converted by rows_to_f16 with a power-of-two row factor
 //     (largest element mapped into [2^14, 2^15)).
 // Every product is exact, the sum is fp32 (as the scalar definition), and the
@@ -76,7 +77,8 @@ constexpr int kAhead = 4;
 // policy (operand 2 = nt) so they do not evict the A tile shared through L2.
 constexpr int kNonTemporal = 2;
 
-constexpr uint32_t kCodeMask = 0x000F000Fu;
+constexpr uint32_t kCodeLo = 0x000F000Fu;   // codes at bits 0-3 of each half
+constexpr uint32_t kCodeHi = 0x00F000F0u;   // codes at bits 4-7 of each half
 constexpr uint32_t kF16_1024 = 0x64006400u;  // fp16 1024.0 in both halves
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
@@ -85,17 +87,35 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
   return r;
 }
 
-// Eight codes of one column block -> fp16 (code - 8) * s, exactly: OR-ing the
-// code into fp16 1024.0 gives 1024 + code, the subtraction of 1032 is exact
-// (small integers), and so is the product with s (4 x 8 significant bits).
-__device__ __forceinline__ f16x8 dequant(uint32_t w, f16x2 s2, uint32_t magic) {
-  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+// Eight codes of one column block -> fp16 (code - 8) * s, exactly. A code at
+// bits 0-3 of a half OR-ed into fp16 1024.0 gives 1024 + code, one at bits 4-7
+// gives 1024 + 16 code (the mantissa's unit is 1 there), so only the upper
+// byte pairs need a shift. Subtracting 1032, resp. 1152, is exact (small
+// integers) and leaves q, resp. 16 q; times s, resp. s / 16, that is q * s
+// exactly. The four extractions, the four subtractions and the four products
+// are independent of one another within each step, so they issue back to
+// back with no dependent packed operation right behind its producer.
+__device__ __forceinline__ f16x8 dequant(uint32_t w, f16x2 s2, f16x2 s2_16, uint32_t magic) {
+  const f16x2 b_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 b_hi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t w8 = w >> 8;
+  f16x2 t0 = __builtin_bit_cast(f16x2, and_or(w, kCodeLo, magic));   // elements 0, 1
+  f16x2 t1 = __builtin_bit_cast(f16x2, and_or(w, kCodeHi, magic));   // elements 2, 3
+  f16x2 t2 = __builtin_bit_cast(f16x2, and_or(w8, kCodeLo, magic));  // elements 4, 5
+  f16x2 t3 = __builtin_bit_cast(f16x2, and_or(w8, kCodeHi, magic));  // elements 6, 7
+  t0 = t0 + b_lo;
+  t1 = t1 + b_hi;
+  t2 = t2 + b_lo;
+  t3 = t3 + b_hi;
+  t0 = t0 * s2;
+  t1 = t1 * s2_16;
+  t2 = t2 * s2;
+  t3 = t3 * s2_16;
   u32x4 r;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const f16x2 t = __builtin_bit_cast(f16x2, and_or(w >> (4 * d), kCodeMask, magic));
-    r[d] = __builtin_bit_cast(uint32_t, (t + bias) * s2);
-  }
+  r[0] = __builtin_bit_cast(uint32_t, t0);
+  r[1] = __builtin_bit_cast(uint32_t, t1);
+  r[2] = __builtin_bit_cast(uint32_t, t2);
+  r[3] = __builtin_bit_cast(uint32_t, t3);
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -207,11 +227,14 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
       sc[j] = *reinterpret_cast<const u32x2*>(base + kABytes + kBBytes + (wn * kStageGroups + j) * 128 +
                                              8 * (lane & 15));
     }
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const auto deq0 = [&](int j) {
-      return dequant(HALF ? nib[j].y : nib[j].x, splat(HALF ? sc[j].x >> 16 : sc[j].x & 0xFFFFu), magic);
+      const f16x2 s2 = splat(HALF ? sc[j].x >> 16 : sc[j].x & 0xFFFFu);
+      return dequant(HALF ? nib[j].y : nib[j].x, s2, s2 * sixteenth, magic);
     };
     const auto deq1 = [&](int j) {
-      return dequant(HALF ? nib[j].w : nib[j].z, splat(HALF ? sc[j].y >> 16 : sc[j].y & 0xFFFFu), magic);
+      const f16x2 s2 = splat(HALF ? sc[j].y >> 16 : sc[j].y & 0xFFFFu);
+      return dequant(HALF ? nib[j].w : nib[j].z, s2, s2 * sixteenth, magic);
     };
     f16x8 a[kRowBlocks];
 #pragma unroll

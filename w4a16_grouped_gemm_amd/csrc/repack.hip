@@ -70,9 +70,11 @@ __global__ void repack_scales_kernel(const uint16_t* __restrict__ s, uint16_t* _
 }
 
 // Normalised fp16 scales and channel exponents: one thread per (expert, packed
-// channel). E_n is the unbiased exponent of the channel's largest |s| (a zero
-// channel gets 0, bf16 subnormals count as 2^-126), and every group scale is
-// stored as fp16(s * 2^-E_n), a value in (-2, 2).
+// channel). E_n is the unbiased exponent of the channel's largest |s| minus 4
+// (a zero channel counts as exponent 0, bf16 subnormals as 2^-126), and every
+// group scale is stored as fp16(s * 2^-E_n), a value in (-32, 32): the largest
+// lands in [16, 32), so s / 16, which the tiled GEMM also uses, keeps the
+// range [1, 2) of the largest and stays exact wherever s is.
 __global__ void repack_f16_scales_kernel(const uint16_t* __restrict__ s, uint16_t* __restrict__ out,
                                          int32_t* __restrict__ col_exp, int N, int K, int interleave_I,
                                          int64_t total) {
@@ -86,7 +88,7 @@ __global__ void repack_f16_scales_kernel(const uint16_t* __restrict__ s, uint16_
     uint32_t mx = 0;
     for (int g = 0; g < G; ++g) mx = max(mx, (uint32_t)(src[g] & 0x7FFFu));
     const int ef = (int)(mx >> 7);
-    const int ex = mx == 0 ? 0 : (ef == 0 ? -126 : ef - 127);
+    const int ex = (mx == 0 ? 0 : (ef == 0 ? -126 : ef - 127)) - 4;
     col_exp[d] = ex;
     for (int g = 0; g < G; ++g) {
       const float v = __builtin_amdgcn_ldexpf(__uint_as_float((uint32_t)src[g] << 16), -ex);
