@@ -344,57 +344,58 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
 // largest magnitude is mapped into [2^14, 2^15), which keeps every element
 // exact unless it is more than 2^38 below that largest one (then it rounds on
 // the fp16 subnormal grid, an error below 2^-39 of the row's largest element).
-// dst[r] = src[r] * 2^-row_exp[r]. One workgroup per row; rows that no GEMM
-// reads are skipped: by token (a resident topk id) or by aligned row (real slot).
-constexpr int kRowRegs = 4;
+// dst[r] = src[r] * 2^-row_exp[r]. One wave per row, four rows per workgroup,
+// no workgroup barrier: the wave reads its row once into registers, takes the
+// largest magnitude with a wave-wide reduction and writes the converted row.
+// Rows that no GEMM reads are skipped: by token (a resident topk id) or by
+// aligned row (real slot).
+constexpr int kRowWaves = 4;
+constexpr int kRowRegs = 16;  // 16-byte chunks per lane held in registers: rows up to 8192 elements
 
 template <bool BY_TOKEN>
-__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ src, int32_t K, int32_t nrows,
-                                                          const int32_t* __restrict__ topk_ids, int32_t topk,
-                                                          int32_t E, const int32_t* __restrict__ sorted,
-                                                          const int32_t* __restrict__ ntpp, int32_t n_slots,
-                                                          uint16_t* __restrict__ dst, int32_t* __restrict__ row_exp) {
-  __shared__ uint32_t red[4];
-  const int tid = (int)threadIdx.x;
+__global__ __launch_bounds__(64 * kRowWaves) void rows_to_f16_kernel(
+    const uint16_t* __restrict__ src, int32_t K, int32_t nrows, const int32_t* __restrict__ topk_ids, int32_t topk,
+    int32_t E, const int32_t* __restrict__ sorted, const int32_t* __restrict__ ntpp, int32_t n_slots,
+    uint16_t* __restrict__ dst, int32_t* __restrict__ row_exp) {
+  const int lane = (int)threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int chunks = K / 8;
   const int live = BY_TOKEN ? nrows : min(*ntpp, nrows);
-  for (int r = (int)blockIdx.x; r < live; r += (int)gridDim.x) {
-    bool need = false;
+  for (int r = (int)blockIdx.x * kRowWaves + wave; r < live; r += (int)gridDim.x * kRowWaves) {
+    bool need;
     if (BY_TOKEN) {
-      for (int j = 0; j < topk; ++j) need |= (unsigned)topk_ids[(int64_t)r * topk + j] < (unsigned)E;
+      // topk <= 64: lane j looks at the token's j-th routed id
+      const int id = lane < topk ? topk_ids[(int64_t)r * topk + lane] : -1;
+      need = __builtin_amdgcn_ballot_w64((unsigned)id < (unsigned)E) != 0;
     } else {
       need = (unsigned)sorted[r] < (unsigned)n_slots;
     }
-    if (!need) continue;  // uniform: every thread read the same values
+    if (!need) continue;  // uniform across the wave
     const u32x4* row = reinterpret_cast<const u32x4*>(src + (int64_t)r * K);
-    // one read of the row: up to kRowRegs 16-byte chunks per thread stay in
-    // registers (rows up to 8192 elements); longer rows re-read the rest
     u32x4 v[kRowRegs];
     // largest |x| as a bf16 bit pattern (sign cleared: integer order = magnitude order)
     uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < kRowRegs; ++i) {
-      const int ch = tid + 256 * i;
-      v[i] = ch < chunks ? row[ch] : u32x4{0, 0, 0, 0};
+      const int ch = lane + 64 * i;
+      v[i] = ch < chunks ? __builtin_nontemporal_load(row + ch) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i)
 #pragma unroll
       for (int d = 0; d < 4; ++d) mx = max(mx, max(v[i][d] & 0x7FFFu, (v[i][d] >> 16) & 0x7FFFu));
-    }
-    for (int ch = tid + 256 * kRowRegs; ch < chunks; ch += 256) {
+    for (int ch = lane + 64 * kRowRegs; ch < chunks; ch += 64) {
       const u32x4 w = row[ch];
 #pragma unroll
       for (int d = 0; d < 4; ++d) mx = max(mx, max(w[d] & 0x7FFFu, (w[d] >> 16) & 0x7FFFu));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
-    __syncthreads();
-    mx = max(max(red[0], red[1]), max(red[2], red[3]));
-    __syncthreads();  // red is reused by the next row
     // unbiased exponent of the largest element (subnormals count as -126)
     const int ef = (int)(mx >> 7);
     const int ex = mx == 0 ? 14 : (ef == 0 ? -126 : ef - 127);
     const int e = ex - 14;
-    if (tid == 0) row_exp[r] = e;
+    if (lane == 0) row_exp[r] = e;
     u32x4* out = reinterpret_cast<u32x4*>(dst + (int64_t)r * K);
     const auto convert = [&](u32x4 w) {
       u32x4 o;
@@ -409,10 +410,10 @@ __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __rest
     };
 #pragma unroll
     for (int i = 0; i < kRowRegs; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = lane + 64 * i;
       if (ch < chunks) out[ch] = convert(v[i]);
     }
-    for (int ch = tid + 256 * kRowRegs; ch < chunks; ch += 256) out[ch] = convert(row[ch]);
+    for (int ch = lane + 64 * kRowRegs; ch < chunks; ch += 64) out[ch] = convert(row[ch]);
   }
 }
 
@@ -456,13 +457,15 @@ namespace {
 int32_t* row_exp_of(void* scratch, int64_t rows, int32_t K) {
   return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(scratch) + ((size_t)rows * K * 2 + 255) / 256 * 256);
 }
-int rows_grid(int64_t rows) { return (int)std::max<int64_t>(1, std::min<int64_t>(rows, (int64_t)device_cu_count() * 16)); }
+int rows_grid(int64_t rows) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>((rows + kRowWaves - 1) / kRowWaves, (int64_t)device_cu_count() * 16));
+}
 }  // namespace
 
 hipError_t launch_rows_to_f16_tokens(const uint16_t* x, int32_t T, int32_t K, const int32_t* topk_ids, int32_t topk,
                                      int32_t E, void* scratch, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_to_f16_kernel<true>, dim3(rows_grid(T)), dim3(256), 0, stream, x, K, T, topk_ids, topk, E,
+  hipLaunchKernelGGL(rows_to_f16_kernel<true>, dim3(rows_grid(T)), dim3(64 * kRowWaves), 0, stream, x, K, T, topk_ids, topk, E,
                      nullptr, nullptr, 0, static_cast<uint16_t*>(scratch), row_exp_of(scratch, T, K));
   return hipGetLastError();
 }
@@ -470,7 +473,7 @@ hipError_t launch_rows_to_f16_tokens(const uint16_t* x, int32_t T, int32_t K, co
 hipError_t launch_rows_to_f16_aligned(const uint16_t* h, int32_t capacity, int32_t K, const int32_t* sorted,
                                       const int32_t* ntpp, int32_t n_slots, void* scratch, hipStream_t stream) {
   if (capacity == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_to_f16_kernel<false>, dim3(rows_grid(capacity)), dim3(256), 0, stream, h, K, capacity,
+  hipLaunchKernelGGL(rows_to_f16_kernel<false>, dim3(rows_grid(capacity)), dim3(64 * kRowWaves), 0, stream, h, K, capacity,
                      nullptr, 0, 0, sorted, ntpp, n_slots, static_cast<uint16_t*>(scratch),
                      row_exp_of(scratch, capacity, K));
   return hipGetLastError();
