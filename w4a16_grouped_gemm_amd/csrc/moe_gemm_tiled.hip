@@ -128,6 +128,37 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Lane quads (lanes 4m .. 4m + 3) transpose a 4 x 4 block: before, lane j
+// holds a[i] = M[i][j]; after, lane j holds a[i] = M[j][i]. Two rounds of DPP
+// quad permutations: swap with lane j ^ 1 the elements whose index differs
+// from j in bit 0, then with lane j ^ 2 those that differ in bit 1.
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ void quad_transpose(float (&a)[4], int lane) {
+  constexpr int kSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+  constexpr int kSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+  const bool odd = lane & 1, hi = lane & 2;
+  {
+    const float t0 = quad_dpp<kSwap1>(a[1]), t1 = quad_dpp<kSwap1>(a[0]);
+    const float t2 = quad_dpp<kSwap1>(a[3]), t3 = quad_dpp<kSwap1>(a[2]);
+    a[0] = odd ? t0 : a[0];
+    a[1] = odd ? a[1] : t1;
+    a[2] = odd ? t2 : a[2];
+    a[3] = odd ? a[3] : t3;
+  }
+  {
+    const float t0 = quad_dpp<kSwap2>(a[2]), t1 = quad_dpp<kSwap2>(a[3]);
+    const float t2 = quad_dpp<kSwap2>(a[0]), t3 = quad_dpp<kSwap2>(a[1]);
+    a[0] = hi ? t0 : a[0];
+    a[1] = hi ? t1 : a[1];
+    a[2] = hi ? a[2] : t2;
+    a[3] = hi ? a[3] : t3;
+  }
+}
+
 __device__ __forceinline__ f16x2 splat(uint32_t bits16) {
   const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
   return f16x2{h, h};
@@ -265,6 +296,36 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
   const int pc0 = nb * kNBlock + 16 * HALF + (lane & 15);
   const int32_t* cexp = p.col_exp + (int64_t)e * p.N;
   const int ce0 = cexp[pc0], ce1 = cexp[pc0 + 32];
+  if (MODE == kDown && !p.out_bf16) {
+    // fp32 rows of y: a 4 x 4 transpose inside each lane quad turns a lane's
+    // four rows of one channel into one row of four consecutive channels, so
+    // each lane stores 16 bytes per row block and column block (a quarter of
+    // the store instructions of one float per row)
+    const int q = lane & 3;
+    float* ybase = static_cast<float*>(p.out) + nb * kNBlock + 16 * HALF + 4 * ((lane & 15) >> 2);
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      float v0[4], v1[4];
+      int ids[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + i;
+        ids[i] = p.sorted[prow];
+        const int re = p.row_exp[prow];  // padding rows: any value, never stored
+        v0[i] = __builtin_amdgcn_ldexpf(acc[rb][0][i], re + ce0);
+        v1[i] = __builtin_amdgcn_ldexpf(acc[rb][1][i], re + ce1);
+      }
+      quad_transpose(v0, lane);
+      quad_transpose(v1, lane);
+      const int id = q == 0 ? ids[0] : q == 1 ? ids[1] : q == 2 ? ids[2] : ids[3];
+      if ((unsigned)id < (unsigned)p.n_slots) {
+        float* y = ybase + (int64_t)id * p.out_ld;
+        *reinterpret_cast<floatx4*>(y) = floatx4{v0[0], v0[1], v0[2], v0[3]};
+        *reinterpret_cast<floatx4*>(y + 32) = floatx4{v1[0], v1[1], v1[2], v1[3]};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) {
 #pragma unroll
