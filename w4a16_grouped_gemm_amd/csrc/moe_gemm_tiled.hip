@@ -326,6 +326,35 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     }
     return;
   }
+  if (MODE == kGateUp) {
+    // h rows: the same quad transpose, four consecutive bf16 channels of one
+    // row per lane in one 8-byte store
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const int q = lane & 3;
+    __bf16* hbase = static_cast<__bf16*>(p.out) + nb * 32 + 16 * HALF + 4 * ((lane & 15) >> 2);
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      float hv[4];
+      bool real[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + i;
+        const int id = p.sorted[prow];
+        real[i] = (unsigned)id < (unsigned)p.n_slots;
+        const int re = real[i] ? p.row_exp[id / p.topk] : 0;  // padding rows: never stored
+        hv[i] = silu_mul(__builtin_amdgcn_ldexpf(acc[rb][0][i], re + ce0),
+                         __builtin_amdgcn_ldexpf(acc[rb][1][i], re + ce1));
+      }
+      quad_transpose(hv, lane);
+      const bool mine = q == 0 ? real[0] : q == 1 ? real[1] : q == 2 ? real[2] : real[3];
+      if (mine) {
+        const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + q;
+        *reinterpret_cast<bf16x4*>(hbase + (int64_t)prow * p.out_ld) =
+            bf16x4{(__bf16)hv[0], (__bf16)hv[1], (__bf16)hv[2], (__bf16)hv[3]};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) {
 #pragma unroll
@@ -411,9 +440,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
 // Rows that no GEMM reads are skipped: by token (a resident topk id) or by
 // aligned row (real slot).
 constexpr int kRowWaves = 4;
-constexpr int kRowRegs = 16;  // 16-byte chunks per lane held in registers: rows up to 8192 elements
+// REGS: 16-byte chunks per lane held in registers (rows up to 512 REGS
+// elements; longer rows re-read the rest). Rows of up to 2048 elements take
+// the 4-register build, whose smaller VGPR budget keeps twice as many waves
+// (rows) in flight.
 
-template <bool BY_TOKEN>
+template <bool BY_TOKEN, int REGS>
 __global__ __launch_bounds__(64 * kRowWaves) void rows_to_f16_kernel(
     const uint16_t* __restrict__ src, int32_t K, int32_t nrows, const int32_t* __restrict__ topk_ids, int32_t topk,
     int32_t E, const int32_t* __restrict__ sorted, const int32_t* __restrict__ ntpp, int32_t n_slots,
@@ -433,19 +465,19 @@ __global__ __launch_bounds__(64 * kRowWaves) void rows_to_f16_kernel(
     }
     if (!need) continue;  // uniform across the wave
     const u32x4* row = reinterpret_cast<const u32x4*>(src + (int64_t)r * K);
-    u32x4 v[kRowRegs];
+    u32x4 v[REGS];
     // largest |x| as a bf16 bit pattern (sign cleared: integer order = magnitude order)
     uint32_t mx = 0;
 #pragma unroll
-    for (int i = 0; i < kRowRegs; ++i) {
+    for (int i = 0; i < REGS; ++i) {
       const int ch = lane + 64 * i;
       v[i] = ch < chunks ? __builtin_nontemporal_load(row + ch) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < kRowRegs; ++i)
+    for (int i = 0; i < REGS; ++i)
 #pragma unroll
       for (int d = 0; d < 4; ++d) mx = max(mx, max(v[i][d] & 0x7FFFu, (v[i][d] >> 16) & 0x7FFFu));
-    for (int ch = lane + 64 * kRowRegs; ch < chunks; ch += 64) {
+    for (int ch = lane + 64 * REGS; ch < chunks; ch += 64) {
       const u32x4 w = row[ch];
 #pragma unroll
       for (int d = 0; d < 4; ++d) mx = max(mx, max(w[d] & 0x7FFFu, (w[d] >> 16) & 0x7FFFu));
@@ -470,11 +502,11 @@ __global__ __launch_bounds__(64 * kRowWaves) void rows_to_f16_kernel(
       return o;
     };
 #pragma unroll
-    for (int i = 0; i < kRowRegs; ++i) {
+    for (int i = 0; i < REGS; ++i) {
       const int ch = lane + 64 * i;
       if (ch < chunks) out[ch] = convert(v[i]);
     }
-    for (int ch = lane + 64 * kRowRegs; ch < chunks; ch += 64) out[ch] = convert(row[ch]);
+    for (int ch = lane + 64 * REGS; ch < chunks; ch += 64) out[ch] = convert(row[ch]);
   }
 }
 
@@ -526,7 +558,8 @@ int rows_grid(int64_t rows) {
 hipError_t launch_rows_to_f16_tokens(const uint16_t* x, int32_t T, int32_t K, const int32_t* topk_ids, int32_t topk,
                                      int32_t E, void* scratch, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_to_f16_kernel<true>, dim3(rows_grid(T)), dim3(64 * kRowWaves), 0, stream, x, K, T, topk_ids, topk, E,
+  const auto kern = K <= 2048 ? rows_to_f16_kernel<true, 4> : rows_to_f16_kernel<true, 16>;
+  hipLaunchKernelGGL(kern, dim3(rows_grid(T)), dim3(64 * kRowWaves), 0, stream, x, K, T, topk_ids, topk, E,
                      nullptr, nullptr, 0, static_cast<uint16_t*>(scratch), row_exp_of(scratch, T, K));
   return hipGetLastError();
 }
@@ -534,7 +567,8 @@ hipError_t launch_rows_to_f16_tokens(const uint16_t* x, int32_t T, int32_t K, co
 hipError_t launch_rows_to_f16_aligned(const uint16_t* h, int32_t capacity, int32_t K, const int32_t* sorted,
                                       const int32_t* ntpp, int32_t n_slots, void* scratch, hipStream_t stream) {
   if (capacity == 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_to_f16_kernel<false>, dim3(rows_grid(capacity)), dim3(64 * kRowWaves), 0, stream, h, K, capacity,
+  const auto kern = K <= 2048 ? rows_to_f16_kernel<false, 4> : rows_to_f16_kernel<false, 16>;
+  hipLaunchKernelGGL(kern, dim3(rows_grid(capacity)), dim3(64 * kRowWaves), 0, stream, h, K, capacity,
                      nullptr, 0, 0, sorted, ntpp, n_slots, static_cast<uint16_t*>(scratch),
                      row_exp_of(scratch, capacity, K));
   return hipGetLastError();
