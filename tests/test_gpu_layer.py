@@ -61,6 +61,41 @@ def test_small_cases(name, T, H, I, E, topk, Eg, bm):
     parity(d.forward(bm), oracle_rows(c), name)
 
 
+def _random_shapes(n=24, seed=2024):
+    """Seeded random layer shapes over every block_m and kernel family: H a
+    multiple of 64 and I of 32 (the supported shapes; some multiples of 256 for
+    the tiled and LDS-ring kernels, some not), ragged token counts, expert
+    slices of a larger routed set."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        bm = int(rng.choice([16, 32, 64, 128]))
+        H = int(64 * rng.integers(1, 17))     # 64 .. 1024
+        I = int(32 * rng.integers(1, 17))     # 32 .. 512
+        if k % 3 == 0:                        # shapes the 256-wide kernels take
+            H, I = 256 * int(rng.integers(1, 5)), 128 * int(rng.integers(1, 5))
+        E = int(rng.integers(1, 65))
+        topk = int(rng.integers(1, min(8, E) + 1))
+        Eg = E + int(rng.integers(0, E + 1))
+        T = int(rng.integers(1, 201))
+        out.append((f"r{k}", T, H, I, E, topk, Eg, bm))
+    return out
+
+
+RANDOM = _random_shapes()
+
+
+@pytest.mark.parametrize("name,T,H,I,E,topk,Eg,bm", RANDOM, ids=[r[0] for r in RANDOM])
+def test_random_shapes(name, T, H, I, E, topk, Eg, bm):
+    say(f"layer random {name}: T={T} H={H} I={I} E={E} topk={topk} Eg={Eg} bm={bm}")
+    c = synthetic.random_case(name, T=T, H=H, I=I, E=E, topk=topk, block_m=bm, seed=1000 + T + H + I + E,
+                              E_global=Eg)
+    d = DeviceCase(c)
+    out = d.forward(bm)
+    parity(out, oracle_rows(c), f"random {name}")
+    assert np.array_equal(out, d.forward(bm)), "run-to-run difference"
+
+
 def test_wide_dynamic_range_block_m_128():
     """Operands outside the fp16 range: activation rows of N(0,1) * 2^(r - 20)
     for r in -24..8 (down to 2^-44, far below fp16's smallest subnormal), gate_up
