@@ -114,6 +114,13 @@ def cpu_baseline(c, target_slots: int):
                                    f"scaled by slots to the whole layer"}}
 
 
+def gemm_dtype(kernel: str) -> str:
+    """The MFMA operand type of a GEMM kernel: the tiled kernel multiplies exact fp16
+    images of the bf16 activations and int4 * scale weights, the streaming kernels
+    bf16 activations and exact bf16 integer weights; both accumulate in fp32."""
+    return "fp16" if kernel == "moe_gemm_tiled_kernel" else "bf16"
+
+
 def gemm_kernel_name(block_m: int, N: int, K: int) -> str:
     """The GEMM kernel the library dispatches to for this block_m and shape."""
     if block_m == 128 and N % 256 == 0 and (K // 32) % 2 == 0:
@@ -241,7 +248,8 @@ def bench_grouped(args, layout: str):
     print(json.dumps({
         "metric": f"W4A16 MoE layer µs, {layout} grouped layout", "value": round(med, 2), "unit": "us",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(med / 1e3, 5),
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": gemm_dtype(gemm_kernel_name(bm, 2 * I, H)), "data": "synthetic",
         "config": {"workload": name, "rows": rows, "block_m": bm, "cache": "cold (1 GiB read before each step)"},
         "layer_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "layer_TFLOPs": round(tflops, 2),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "alg_bytes": layer_bytes, "alg_flops": layer_flops,
@@ -458,7 +466,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": (gemm_dtype(gemm_kernel_name(128, 2 * I, H)) + "+" + gemm_dtype(gemm_kernel_name(16, 2 * I, H))
+                  if split else gemm_dtype(gemm_kernel_name(bm, 2 * I, H))),
         "data": "synthetic",
         "config": {"workload": c.name, "T": T, "hidden": H, "intermediate": I, "experts_local": E,
                    "experts_global": Eg, "topk": topk, "block_m": bm if not split else f"128 / 16 split at {split} slots",
