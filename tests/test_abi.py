@@ -159,7 +159,7 @@ def test_validation_status_codes(lib):
     assert sp(lcap=127) == 3
     assert sp(hcap=2**31 - 100, lcap=200) == 3             # joined array beyond int32
     kimi = w.make_shape(48, 7168, 2048)
-    assert w.w4a16_moe_routed_split(kimi, 16384, 8, 384) == 32     # prefill: heavy experts from 32 slots
+    assert w.w4a16_moe_routed_split(kimi, 16384, 8, 384) == 17     # prefill: heavy experts from 17 slots
     assert w.w4a16_moe_routed_split(kimi, 128, 8, 384) == 0        # decode: one alignment
     assert w.w4a16_moe_routed_split(kimi, 128, 8, 40) == -1        # fewer global than local experts
     need = w.w4a16_moe_routed_workspace_bytes(kimi, 16384, 8, 384)

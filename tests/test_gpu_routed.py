@@ -113,8 +113,8 @@ def test_routed_small_skewed(T, topk, E, Eg, s):
     ids = c.topk_ids
     cnt = np.bincount(ids[ids < c.E], minlength=c.E)
     d = DeviceCase(c)
-    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg) == 32
-    assert (cnt >= 32).any() and ((cnt > 0) & (cnt < 32)).any(), cnt
+    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg) == 17
+    assert (cnt >= 17).any() and ((cnt > 0) & (cnt < 17)).any(), cnt
     say(f"routed small T={T}: counts {cnt.tolist()}")
     out = routed(d, Eg)
     ref = oracle.moe_layer(c.x, c.topk_ids, c.topk_weights, c.w13_q, c.w13_s, c.w2_q, c.w2_s, c.E, c.I)

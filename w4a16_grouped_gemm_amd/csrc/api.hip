@@ -511,8 +511,16 @@ namespace {
 // block_m. (Running the light set on a second stream, next to the heavy
 // tiles, was measured: both kernels slowed down by about what they overlapped,
 // so the sets run one after the other on the caller's stream.)
-constexpr int32_t kHeavyRows = 32;
+// The threshold is one more than the light block size: every light expert
+// then fits one 16-row block and streams its weights once. Experts with 17 to
+// 31 slots cost about as much either way by a per-expert model (two weight
+// streams against one mostly padded 128-row tile row), and on the tiled side
+// they mostly fill resident slots that the heavy launch leaves idle (the
+// skewed 48-expert prefill: heavy set 25 -> 30 row blocks, still one round of
+// tiles; light set 24 -> 14 row blocks; layer 543 -> 521 us, against 538 us
+// at a threshold of 24 and 543 us at 32).
 constexpr int32_t kLightBlockM = 16;
+constexpr int32_t kHeavyRows = kLightBlockM + 1;
 constexpr int32_t kHeavyBlockM = 128;
 
 struct AlignSet {
