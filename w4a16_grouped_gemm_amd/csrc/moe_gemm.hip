@@ -256,12 +256,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int t = (int)blockIdx.x / chunks;
   const int c0 = ((int)blockIdx.x - t * chunks) * cols;
   const int c1 = min(H, c0 + cols);
+  // the token's resident slots as a bit mask (topk <= 32): lane j of every
+  // wave reads routed id j once, so a row without a resident slot is stores only
+  const int lane = (int)threadIdx.x & 63;
+  const int my_id = lane < topk ? ids[(int64_t)t * topk + lane] : -1;
+  const uint64_t resident = __ballot((unsigned)my_id < (unsigned)E);
   for (int n0 = c0 + 8 * (int)threadIdx.x; n0 < c1; n0 += 8 * 256) {
     floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < topk; ++j) {
-      const int slot = t * topk + j;
-      const int e = ids[slot];
-      if ((unsigned)e >= (unsigned)E) continue;
+    for (uint64_t m = resident; m; m &= m - 1) {  // resident slots in j order
+      const int slot = t * topk + __builtin_ctzll(m);
       const float wt = w[slot];
       const floatx4* src = reinterpret_cast<const floatx4*>(y + (int64_t)slot * H + n0);
       lo += wt * src[0];
