@@ -97,21 +97,24 @@ def cpu_baseline(c, target_slots: int):
                          tokens=sample)
         return time.perf_counter() - t0
 
-    dt = timed(tokens)
+    runs = sorted(timed(tokens) for _ in range(3))
+    dt = runs[1]  # median of 3
     # one core on an eighth of the sample (the same tokens' first eighth), scaled the same way
     few = tokens[:max(1, len(tokens) // 8)]
     few_slots = int(local[few].sum())
     oracle.set_num_threads(1)
     try:
-        dt1 = timed(few)
+        runs1 = sorted(timed(few) for _ in range(3))
     finally:
         oracle.set_num_threads(cores)
+    dt1 = runs1[1]
     return {"value": round(dt / slots * S * 1e6, 1), "unit": "us", "cores": cores, "kind": "oracle",
-            "sample": f"{len(tokens)} tokens / {slots} resident slots of {c.name} ({S} slots), "
-                      f"{dt:.2f} s wall, scaled by slots to the whole layer",
+            "sample": f"{len(tokens)} tokens / {slots} resident slots of {c.name} ({S} slots), median of 3 runs "
+                      f"({', '.join(f'{r:.2f}' for r in runs)} s wall), scaled by slots to the whole layer",
             "one_core": {"value": round(dt1 / few_slots * S * 1e6, 1), "unit": "us", "cores": 1,
-                         "sample": f"{len(few)} tokens / {few_slots} resident slots, {dt1:.2f} s wall, "
-                                   f"scaled by slots to the whole layer"}}
+                         "sample": f"{len(few)} tokens / {few_slots} resident slots, median of 3 runs "
+                                   f"({', '.join(f'{r:.2f}' for r in runs1)} s wall), scaled by slots to the "
+                                   f"whole layer"}}
 
 
 def gemm_dtype(kernel: str) -> str:
@@ -257,43 +260,115 @@ def bench_grouped(args, layout: str):
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    # the MFMA-bound prefill layers run ~20% slow for ~15 ms after the GPU comes out of idle (clock and
-    # power settling, seen in kernel traces); 30 untimed steps cover that, a few ms of GPU time
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--block-m", type=int, default=0, help="0: the tokens-per-expert heuristic")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-router", action="store_true", help="skip the router + alignment timing")
-    ap.add_argument("--layout", default="routed", choices=["routed", "contiguous", "masked"],
-                    help="routed: the layer on top-k routed ids (the default line); contiguous / masked: "
-                         "the grouped-layout entry points")
-    ap.add_argument("--cpu-slots", type=int, default=3000,
-                    help="resident slots the CPU baseline computes (all of them when the layer has fewer)")
-    ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the layer here is one GPU's expert or intermediate slice "
-              "and no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
+def bench_sweep(args):
+    """Tokens-per-expert sweep on the 48-expert Kimi-K2 slice (H 7168, I 2048; the decode workload's
+    weights): for T = 1, 2, 4, ..., 8192 tokens routed top-8 over 384 experts from N(0,1) logits
+    (experts 0-47 resident), the layer timed at every block_m through moe_align + w4a16_moe_forward,
+    and the one-call routed layer with its own choice. The pages measure kernels at every power of two
+    of M from 1 to 8192 tokens (Humming announcement, "결과: 커널 마이크로벤치마크") and pick the tile by
+    routed tokens per expert (Chord page, "인덱스 커널 기법"). One JSON line per T."""
     import torch
 
     import synthetic
     import w4a16_grouped_gemm_amd as w
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    w.load()  # fail loudly if the HIP library is not built
-    if args.layout != "routed":
-        return bench_grouped(args, args.layout)
-    print(f"[bench] building {args.workload}", file=sys.stderr, flush=True)
-    c = synthetic.workload(args.workload)
+    E, H, I, topk, Eg = 48, synthetic.KIMI_H, synthetic.KIMI_I, synthetic.KIMI_TOPK, synthetic.KIMI_E
+    shape = w.make_shape(E, H, I)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).cuda()
+
+    print("[bench] sweep: building the 48-expert slice", file=sys.stderr, flush=True)
+    w13_q, w13_s, w2_q, w2_s = synthetic.make_weights(E, H, I, 202)
+    n13, n2 = w.w4a16_packed_bytes(shape)
+    w13p = torch.empty(n13, dtype=torch.uint8, device="cuda")
+    w2p = torch.empty(n2, dtype=torch.uint8, device="cuda")
+    w.w4a16_repack(shape, dev(w13_q), dev(w13_s), dev(w2_q), dev(w2_s), w13p, w2p)
+    torch.cuda.synchronize()
+    del w13_q, w13_s, w2_q, w2_s
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def timeit(step, steps):
+        for _ in range(3):
+            flush_buf.sum()
+            step()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            flush_buf.sum()
+            a, b = mk()
+            a.record()
+            step()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+    # clock settling before the first point
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_ms / 1e3:
+        flush_buf.sum()
+        torch.cuda.synchronize()
+    rows = []
+    for lt in range(14):
+        T = 1 << lt
+        c = synthetic.random_case(f"sweep_T{T}", T=T, H=H, I=I, E=E, topk=topk, block_m=16, seed=500 + lt,
+                                  E_global=Eg, weights=False)
+        c.x = synthetic.make_x(T, H, 600 + lt)
+        work = algorithmic_work(c)
+        x, ids, wts = dev(c.x), dev(c.topk_ids.astype(np.int32)), dev(c.topk_weights.astype(np.float32))
+        out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        pt = {"T": T, "tok_e": round(T * topk / Eg, 3), "resident_slots": work["S"], "active_experts": work["active"]}
+        us = {}
+        for bm in (16, 32, 64, 128):
+            buf = w.align_buffers(T, topk, E, bm)
+            ws = torch.empty(w.w4a16_moe_workspace_bytes(shape, T, topk, bm), dtype=torch.uint8, device="cuda")
+
+            def step(bm=bm, buf=buf, ws=ws):
+                w.moe_align(ids, E, bm, buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"],
+                            None, buf["workspace"])
+                w.w4a16_moe_forward(shape, x, ids, wts, buf["sorted_token_ids"], buf["expert_ids"],
+                                    buf["num_tokens_post_padded"], bm, w13p, w2p, out, ws)
+            us[bm] = round(timeit(step, args.steps), 2)
+            del ws, buf
+        wsr = torch.empty(w.w4a16_moe_routed_workspace_bytes(shape, T, topk, Eg), dtype=torch.uint8, device="cuda")
+        routed_us = round(timeit(lambda: w.w4a16_moe_routed_forward(shape, x, ids, wts, Eg, w13p, w2p, out, wsr),
+                                 args.steps), 2)
+        del wsr
+        best = min(us, key=us.get)
+        t_hbm = work["layer_bytes"] / (HBM_PEAK_GBPS * 1e9) * 1e6
+        t_mfma = work["layer_flops"] / (BF16_PEAK_TFLOPS * 1e12) * 1e6
+        pt.update({"layer_us_by_block_m": {str(k): v for k, v in us.items()}, "best_block_m": best,
+                   "chosen_block_m": w.w4a16_choose_block_m(T, topk, E, Eg),
+                   "routed_split": w.w4a16_moe_routed_split(shape, T, topk, Eg), "routed_us": routed_us,
+                   "binding": "hbm" if t_hbm >= t_mfma else "mfma",
+                   "routed_roofline_frac": round(max(t_hbm, t_mfma) / routed_us, 4),
+                   "best_roofline_frac": round(max(t_hbm, t_mfma) / us[best], 4)})
+        rows.append(pt)
+        print(json.dumps(pt), flush=True)
+    return rows
+
+
+# Workloads the default run also times, after the headline one, each in this process with its own
+# warm-up: the intermediate slice (HBM-bound) and the two prefill layers (MFMA-bound).
+EXTRA_WORKLOADS = ("islice_tp8", "prefill_contig48", "prefill_skew48")
+
+
+def bench_routed(args, workload: str, steps: int, warmup: int, settle_ms: float, with_cpu: bool,
+                 with_router: bool, with_traffic: bool = True):
+    """Time one routed workload: one call of the layer per step (alignment included), then a staged
+    replica for the per-kernel breakdown. Returns the result dict of the JSON line."""
+    import torch
+
+    import synthetic
+    import w4a16_grouped_gemm_amd as w
+
+    print(f"[bench] building {workload}", file=sys.stderr, flush=True)
+    c = synthetic.workload(workload)
     E, H, I, T, topk = c.E, c.H, c.I, c.T, c.topk
     Eg = c.meta.get("E_global", E)
     bm = args.block_m or w.w4a16_choose_block_m(T, topk, E, Eg)
@@ -401,18 +476,30 @@ def main():
     torch.cuda.synchronize()
     assert torch.equal(ref, out), "staged sequence differs from the one-call layer"
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         if not args.warm:
             flush()
         forward_step(mk(2))
         stages(mk(nev))
     torch.cuda.synchronize()
+    # Clock and power settling: the MFMA-bound layers run ~20% slow for ~15 ms after the GPU
+    # leaves idle (kernel traces), so untimed layers keep it busy for settle_ms of wall time
+    # whatever the warm-up count, synchronising every few steps so the time is GPU time.
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(4):
+            if not args.warm:
+                flush()
+            forward_step(mk(2))
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settled_ms = (time.perf_counter() - t_settle) * 1e3
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timing {steps} steps of {workload}", file=sys.stderr, flush=True)
     layer_ev, stage_ev = [], []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         if not args.warm:
             flush()
         ev = mk(2)
@@ -420,7 +507,7 @@ def main():
         layer_ev.append(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for i in range(args.steps):
+    for i in range(steps):
         if not args.warm:
             flush()
         ev = mk(nev)
@@ -428,7 +515,7 @@ def main():
         stage_ev.append(ev)
     torch.cuda.synchronize()
 
-    route_us = route_align_timing(w, synthetic, dev, c, bm) if not args.no_router else None
+    route_us = route_align_timing(w, synthetic, dev, c, bm) if with_router else None
 
     layer_us = np.array([a.elapsed_time(b) * 1e3 for a, b in layer_ev])
     st = np.array([[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(len(names))] for ev in stage_ev])
@@ -453,15 +540,21 @@ def main():
     if split:
         roof["kernel"] = (gemm_kernel_name(128, 2 * I, H) + f" (gate_up, experts with >= {split} slots) + "
                           + gemm_kernel_name(16, 2 * I, H) + " (gate_up, lighter experts)")
-    roof["traffic"] = stored_traffic(args.workload, "gate_up")
+    roof["traffic"] = stored_traffic(workload, "gate_up") if with_traffic else None
+    # the whole layer against its binding roofline: the larger of the HBM time of its algorithmic
+    # bytes and the MFMA time of its algorithmic flops, over the measured layer time
+    t_hbm = work["layer_bytes"] / (HBM_PEAK_GBPS * 1e9) * 1e6
+    t_mfma = work["layer_flops"] / (BF16_PEAK_TFLOPS * 1e12) * 1e6
+    layer_roof = {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "frac": round(max(t_hbm, t_mfma) / med, 4),
+                  "t_hbm_us": round(t_hbm, 1), "t_mfma_us": round(t_mfma, 1)}
 
     result = {
         "metric": "W4A16 MoE layer µs; decode HBM GB/s, prefill TFLOPS as % of MI355X roofline",
         "value": round(med, 2),
         "unit": "us",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(med / 1e3, 5),
         "higher_is_better": False,
         "scaling": "weak",
@@ -477,29 +570,86 @@ def main():
         "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
         "layer_TFLOPs": round(layer_tflops, 2),
         "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
+        "layer_roofline": layer_roof,
         "kernels_us": kus,
         "layer_us_p10_p90": [round(float(np.percentile(layer_us, 10)), 2), round(float(np.percentile(layer_us, 90)), 2)],
-        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "wall_ms_per_step_incl_flush": round(wall / steps * 1e3, 4),
+        "settle": {"ms": round(settled_ms, 1), "steps": settle_steps},
         "alg_bytes": work["layer_bytes"],
         "alg_flops": work["layer_flops"],
         "roofline": roof,
         "route_align_us": route_us,
-        "targets": {"decode_hbm_frac": 0.70, "prefill_mfma_frac": 0.50},
-        "context": "pages' per-layer speedups of NVIDIA kernels (Chord vs Humming): 1.11-1.33x on H200, "
-                   "1.81-2.15x on B300; context only, not a target on this GPU",
-        "source_hash": kernel_source_hash(),
     }
+    if with_cpu:
+        print(f"[bench] cpu baseline (oracle) on {workload}", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(c, args.cpu_slots)
+    del w13p, w2p, ws, hs, y, scratch, flush_buf
+    torch.cuda.empty_cache()
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed layers for at least this much wall time after the warm-up steps (clock settling)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--only", action="store_true",
+                    help="time only --workload (by default the decode line also carries the other workloads)")
+    ap.add_argument("--block-m", type=int, default=0, help="0: the tokens-per-expert heuristic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-router", action="store_true", help="skip the router + alignment timing")
+    ap.add_argument("--layout", default="routed", choices=["routed", "contiguous", "masked"],
+                    help="routed: the layer on top-k routed ids (the default line); contiguous / masked: "
+                         "the grouped-layout entry points")
+    ap.add_argument("--cpu-slots", type=int, default=3000,
+                    help="resident slots the CPU baseline computes (all of them when the layer has fewer)")
+    ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="tokens-per-expert sweep on the 48-expert slice: T = 1 .. 8192, every block_m")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the layer here is one GPU's expert or intermediate slice "
+              "and no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import w4a16_grouped_gemm_amd as w
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w.load()  # fail loudly if the HIP library is not built
+    if args.layout != "routed":
+        return bench_grouped(args, args.layout)
+    if args.sweep:
+        return bench_sweep(args)
+    result = bench_routed(args, args.workload, args.steps, args.warmup, args.settle_ms,
+                          with_cpu=not args.no_cpu_baseline, with_router=not args.no_router)
+    result["targets"] = {"decode_hbm_frac": 0.70, "prefill_mfma_frac": 0.50}
+    result["context"] = ("pages' per-layer speedups of NVIDIA kernels (Chord vs Humming): 1.11-1.33x on H200, "
+                         "1.81-2.15x on B300; context only, not a target on this GPU")
+    result["source_hash"] = kernel_source_hash()
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        flush()
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = 1 << 28
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(c, args.cpu_slots)
+    if args.workload == DEFAULT_WORKLOAD and not args.only and not args.block_m:
+        # the other workloads of the metric, each timed the same way in this process: their
+        # medians, spreads, rooflines and per-kernel breakdowns (the line's value stays decode's)
+        keep = ("value", "layer_us_p10_p90", "roofline", "layer_roofline", "hbm_frac", "mfma_frac", "kernels_us",
+                "settle", "config", "dtype", "alg_bytes", "alg_flops")
+        result["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            r = bench_routed(args, name, args.steps, args.warmup, args.settle_ms, with_cpu=False, with_router=False)
+            result["workloads"][name] = {k: r[k] for k in keep}
     print(json.dumps(result), flush=True)
 
 

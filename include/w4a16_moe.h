@@ -273,8 +273,10 @@ int w4a16_moe_forward(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T
  *   buffer). These stages write the activation side: every x row of a token
  *   with a resident slot (prepare_x) and every real row of h (prepare_h) as
  *   fp16(row * 2^-e) with e chosen per row so that its largest magnitude lands
- *   in [2^14, 2^15), plus e. Exact except for elements more than 2^38 below
- *   their row's largest, which round to the fp16 subnormal grid. No-ops for
+ *   in [2^14, 2^15), plus e. Exact except for elements more than 2^31 below
+ *   their row's largest (fp16 holds a bf16 value exactly down to 2^-17), which
+ *   round to the fp16 subnormal grid: an absolute error of at most 2^-39 of the
+ *   row's largest element. No-ops for
  *   the other block_m values.
  * gate_up: h[p, c] = bf16(silu(g[p, c]) * g[p, I + c]) for every real row p of
  *   the aligned order (sorted_token_ids[p] < T*topk), g = x[sorted[p]/topk] . W13^T.

@@ -2,9 +2,9 @@
 
 Test infrastructure: it exists to cross-check ``w4a16_moe_oracle.c``. It
 decodes nibbles with explicit bit operations, dequantizes whole weight tensors
-in numpy fp64, and uses library matmuls per slot. Rounding of h to bf16 uses
-torch's float32 -> bfloat16 conversion (round-to-nearest-even) after an fp32
-cast, which matches a direct rounding except at rare double-rounding ties.
+in numpy fp64, and uses library matmuls per slot. h is rounded to bf16
+directly from fp64, round-to-nearest-even on the integer bit pattern
+(round_bf16_f64), not through an fp32 cast.
 """
 from __future__ import annotations
 

@@ -88,3 +88,59 @@ def parity(gpu_bits: np.ndarray, ref: np.ndarray, what: str, row_floor: bool = F
     say(f"  parity {what}: max err/tol {ratio:.4f}, fails {nfail}/{err.size}")
     assert nfail == 0 and np.all(np.isfinite(g)), f"{what}: {nfail} elements out of tolerance, e.g. {bad}"
     return ratio
+
+
+def run_stages(d, bm, srt, eid, ntpp, T, topk, row_ids=None, x=None):
+    """The layer's GEMM stages one by one on the given alignment buffers: returns
+    the GPU's h [capacity, I] (int16 bits) and y [T*topk, H] fp32 as torch tensors.
+    row_ids: the per-token routed ids the prepare stage reads (default d.ids)."""
+    c = d.case
+    x = d.x if x is None else x
+    row_ids = d.ids if row_ids is None else row_ids
+    cap = srt.numel()
+    h = torch.zeros((cap, c.I), dtype=torch.int16, device="cuda")
+    y = torch.zeros((T * topk, c.H), dtype=torch.float32, device="cuda")
+    nws = w.w4a16_moe_stage_workspace_bytes(d.shape, T, topk, bm)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
+    w.w4a16_moe_prepare_x(d.shape, x, row_ids, bm, ws)
+    w.w4a16_moe_gate_up(d.shape, x, T, topk, srt, eid, ntpp, bm, d.w13p, h, ws)
+    w.w4a16_moe_prepare_h(d.shape, T, topk, h, srt, ntpp, bm, ws)
+    w.w4a16_moe_down(d.shape, T, topk, h, srt, eid, ntpp, bm, d.w2p, y, ws)
+    torch.cuda.synchronize()
+    return h, y
+
+
+def check_own_rows(c, x_bits, h, y, srt, eid, ntpp, bm, topk, what):
+    """Each GEMM stage on the very rows it was given, for every real aligned row:
+    h = bf16(silu(g) * u) against g, u the exact fp64 projections of the row's
+    activation (within bf16 rounding plus the fp32 sum's error), and y against
+    the exact fp64 projection of the GPU's own h row. Returns (rows, slots, experts,
+    h rows as bf16 bits, number of h elements whose bf16 rounding differs from
+    the exact value's)."""
+    import oracle
+
+    I, H = c.I, c.H
+    n = int(ntpp.item())
+    s = srt.cpu().numpy()[:n]
+    rows = np.nonzero(s < x_bits.shape[0] * topk)[0]
+    slot = s[rows]
+    ex = eid.cpu().numpy()[rows // bm]
+    g = oracle.expert_rows(x_bits[slot // topk], ex, c.w13_q, c.w13_s, 2 * I, H)
+    h_exact = g[:, :I] / (1.0 + np.exp(-g[:, :I])) * g[:, I:]
+    h_bits = h.cpu().numpy()[rows].view(np.uint16)
+    h_gpu = bf16_to_f64(h_bits)
+    err = np.abs(h_gpu - h_exact)
+    tol = 2.0**-6 * np.abs(h_exact) + 1e-4
+    say(f"  {what} gate_up rows ({len(rows)}): max err/tol {float((err / tol).max()):.4f}")
+    assert np.all(err <= tol), f"{what}: gate_up rows off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
+    import synthetic
+
+    flips = int((h_bits != synthetic.to_bf16_bits(h_exact.astype(np.float32))).sum())
+    y_ref = oracle.expert_rows(h_bits, ex, c.w2_q, c.w2_s, H, I)
+    y_gpu = y.cpu().numpy()[slot].astype(np.float64)
+    err = np.abs(y_gpu - y_ref)
+    tol = 1e-4 * (np.abs(y_ref) + np.abs(y_ref).max(axis=1, keepdims=True))
+    say(f"  {what} down rows: max err/tol {float((err / tol).max()):.4f}; "
+        f"h elements rounded to the other bf16 neighbour than the exact value: {flips}/{h_bits.size}")
+    assert np.all(err <= tol), f"{what}: down rows off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
+    return rows, slot, ex, h_bits, flips

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synthetic
-from _gpu import DeviceCase, bf16_to_f64, parity, say, to_dev
+from _gpu import DeviceCase, bf16_to_f64, check_own_rows, parity, run_stages, say, to_dev
 
 import w4a16_grouped_gemm_amd as w
 
@@ -260,3 +260,31 @@ def test_full_size_sampled(name):
     assert np.all(out[none] == 0)
     d2 = d.forward(c.block_m)
     assert np.array_equal(out, d2), "run-to-run difference"
+
+
+def test_split_k_several_units_per_workgroup():
+    """block_m 16 at the Kimi-K2 shapes (both reductions split between two waves per
+    n-block) with far more live units than the persistent grid's workgroups: 400
+    tokens routed top-8 over 48 local experts give about 240 row blocks, so each
+    workgroup runs two (gate_up) or four (down) units one after the other, and the
+    LDS that held one unit's partial-sum exchange is the next unit's A ring. Every
+    real row of both GEMMs is checked on its own inputs, the layer on sampled
+    tokens, and two runs are compared bit for bit."""
+    c = synthetic.random_case("split_units", T=400, H=7168, I=2048, E=48, topk=8, block_m=16, seed=41)
+    d = DeviceCase(c)
+    bm = 16
+    buf = d.align(bm)
+    srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+    n = int(ntpp.item())
+    say(f"layer split-K, several units per workgroup: {n // bm} row blocks, "
+        f"{n // bm * 32} gate_up units, {n // bm * 56} down units")
+    assert n // bm * 32 > 4096  # more units than 256 CUs x 4 workgroups x 4
+    h, y = run_stages(d, bm, srt, eid, ntpp, c.T, c.topk)
+    check_own_rows(c, c.x, h, y, srt, eid, ntpp, bm, c.topk, "split-K units")
+    out = d.forward(bm)
+    rng = np.random.default_rng(5)
+    tokens = np.array(sorted(set(rng.choice(c.T, size=10, replace=False).tolist()) | {0, c.T - 1}), np.int32)
+    parity(out[tokens], oracle_rows(c, tokens=tokens), f"split-K units ({len(tokens)} sampled tokens)")
+    assert np.array_equal(out, d.forward(bm)), "run-to-run difference"
+    h2, y2 = run_stages(d, bm, srt, eid, ntpp, c.T, c.topk)
+    assert torch.equal(h, h2) and torch.equal(y, y2), "stage run-to-run difference"

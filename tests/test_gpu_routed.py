@@ -181,3 +181,39 @@ def test_routed_full_size_skewed_sampled():
                            tokens=tokens)
     parity(out[tokens], ref, f"routed prefill_skew48 ({len(tokens)} sampled tokens)")
     assert np.all(out[none] == 0)
+
+
+def test_routed_full_size_skewed_identity_sampled():
+    """The heavily skewed prefill (Zipf ranks in expert order: all 48 local experts
+    heavy, 127,817 resident slots, about 1,000 row blocks of 128, several rounds of
+    tiles per workgroup). Sampled: the tokens of the last slots of the busiest
+    experts (their last, partly filled row blocks), tokens from the last row blocks
+    of the whole call (the last tiles the persistent grid runs), the first slot of
+    an expert, tokens without a resident slot and random others."""
+    c = synthetic.workload("prefill_skew48_identity")
+    d = DeviceCase(c)
+    Eg = c.meta["E_global"]
+    local = (c.topk_ids >= 0) & (c.topk_ids < c.E)
+    cnt = np.bincount(c.topk_ids[local], minlength=c.E)
+    say(f"routed full-size prefill_skew48_identity: T={c.T} slots={int(cnt.sum())} "
+        f"split={w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg)} counts {cnt.min()}..{cnt.max()}")
+    out = routed(d, Eg)
+    flat = c.topk_ids.reshape(-1)
+    pick = set()
+    for e in np.argsort(-cnt, kind="stable")[:3]:      # busiest experts: their last slots
+        sl = np.nonzero(flat == e)[0]
+        pick |= set((sl[-3:] // c.topk).tolist())
+    last_e = int(np.nonzero(cnt)[0][-1])                # the last expert's last row block
+    sl = np.nonzero(flat == last_e)[0]
+    nb = (len(sl) - 1) // 128
+    pick |= set((sl[nb * 128:][[0, -1]] // c.topk).tolist())
+    pick |= {int(np.nonzero(flat == 0)[0][0] // c.topk)}   # the first slot of the first expert
+    none = np.nonzero(local.sum(axis=1) == 0)[0]
+    rng = np.random.default_rng(8)
+    pick |= set(none[:2].tolist()) | set(rng.choice(c.T, size=6, replace=False).tolist())
+    tokens = np.array(sorted(pick), np.int32)
+    ref = oracle.moe_layer(c.x, c.topk_ids, c.topk_weights, c.w13_q, c.w13_s, c.w2_q, c.w2_s, c.E, c.I,
+                           tokens=tokens)
+    parity(out[tokens], ref, f"routed prefill_skew48_identity ({len(tokens)} sampled tokens)")
+    assert np.all(out[none] == 0)
+    assert np.array_equal(out, routed(d, Eg)), "run-to-run difference"

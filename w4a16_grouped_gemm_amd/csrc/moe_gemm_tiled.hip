@@ -21,8 +21,9 @@
 // Every product is exact, the sum is fp32 (as the scalar definition), and the
 // epilogue restores 2^(row exponent + E_n) with one ldexp per output. No
 // per-group rescale is needed: the group scale lives in the B operand.
-// The one approximation is fp16's subnormal floor: an activation more than 2^38
-// below its row's largest, or a scale more than 2^17 below its channel's
+// The one approximation is fp16's subnormal floor: an activation more than 2^31
+// below its row's largest (a bf16 value, 8 significant bits, is exact in fp16
+// down to 2^-17), or a scale more than 2^17 below its channel's
 // largest, is rounded to the fp16 subnormal grid (absolute error at most 2^-39
 // of the row's largest element, resp. 2^-25 of the channel's largest scale),
 // far below the rounding of the fp32 sum itself. SiLU's exponential tail puts
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
 
 // Rows of a bf16 matrix -> fp16 with a power-of-two factor per row: the row's
 // largest magnitude is mapped into [2^14, 2^15), which keeps every element
-// exact unless it is more than 2^38 below that largest one (then it rounds on
+// exact unless it is more than 2^31 below that largest one (then it rounds on
 // the fp16 subnormal grid, an error below 2^-39 of the row's largest element).
 // dst[r] = src[r] * 2^-row_exp[r]. One wave per row, four rows per workgroup,
 // no workgroup barrier: the wave reads its row once into registers, takes the
