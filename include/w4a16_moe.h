@@ -120,8 +120,11 @@ size_t moe_align_workspace_bytes(int32_t T, int32_t topk, int32_t num_experts, i
 
 /* block_m for a call, from the expected routed tokens per expert (tok_e =
  * T*topk/E_global): a tile sized by tokens-per-expert, not by total tokens
- * (Chord page, "핵심 기여" and "인덱스 커널 기법": tok_e heuristic). Returns one
- * of 16, 32, 64, 128; 0 for invalid arguments. */
+ * (Chord page, "핵심 기여" and "인덱스 커널 기법": tok_e heuristic): 16 up to
+ * tok_e 6, 32 up to 40, else 128 (thresholds from a measured sweep of the
+ * layer at every block_m over T = 1 .. 8192 on a 48-expert Kimi-K2 slice).
+ * Returns 16, 32 or 128 (64 stays available to callers that pass it); 0 for
+ * invalid arguments. */
 int32_t w4a16_choose_block_m(int32_t T, int32_t topk, int32_t num_experts_local, int32_t num_experts_global);
 
 /* Group the T*topk routed slots by expert, each expert padded to a multiple of

@@ -68,6 +68,9 @@ def test_sizes_and_heuristic(lib):
     assert w.w4a16_choose_block_m(768, 8, 48, 48) == 128
     assert w.w4a16_choose_block_m(16384, 8, 48, 384) == 128
     assert w.w4a16_choose_block_m(1, 8, 48, 384) == 16
+    assert w.w4a16_choose_block_m(1024, 8, 48, 384) == 32   # tok_e 21: 32 rows (64 measured 37% slower)
+    assert w.w4a16_choose_block_m(1920, 8, 48, 384) == 32   # tok_e 40
+    assert w.w4a16_choose_block_m(1944, 8, 48, 384) == 128  # tok_e 40.5
     assert w.w4a16_choose_block_m(8, 8, 48, 8) == 0  # local > global
 
 
@@ -140,7 +143,8 @@ def test_validation_status_codes(lib):
                                         None) == 4
     # masked block_m: the tokens-per-expert rule on expected_m, halved until it divides max_m
     assert w.w4a16_moe_masked_block_m(32, 32) == 32
-    assert w.w4a16_moe_masked_block_m(256, 32) == 64
+    assert w.w4a16_moe_masked_block_m(256, 32) == 32
+    assert w.w4a16_moe_masked_block_m(64, 200) == 64       # 128 halved to divide max_m
     assert w.w4a16_moe_masked_block_m(256, 200) == 128
     assert w.w4a16_moe_masked_block_m(48, 4) == 16
     assert w.w4a16_moe_masked_block_m(40, 4) == 0          # not a multiple of 16
