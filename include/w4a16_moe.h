@@ -14,6 +14,7 @@
  *   moe_route_align     router logits -> top-k ids and weights, then moe_align
  *   w4a16_moe_forward   gate_up GEMM + SiLU-and-mul, down GEMM, top-k weighted combine
  *   w4a16_moe_routed_forward  alignment + the layer in one call, per-expert tile sizes
+ *   w4a16_moe_routed_forward_noalloc  the same with its workspace in a static device array
  *   w4a16_moe_contiguous_forward / w4a16_moe_masked_forward
  *                       the layer on expert-grouped activation layouts
  *   w4a16_repack        once at weight load: canonical int4 + scales -> kernel layout
@@ -57,7 +58,8 @@ typedef enum {
   W4A16_ERR_UNSUPPORTED = 2, /* a valid request outside what the kernels implement */
   W4A16_ERR_CAPACITY = 3,    /* sorted_token_ids buffer shorter than moe_align_capacity */
   W4A16_ERR_WORKSPACE = 4,   /* workspace smaller than the matching *_workspace_bytes */
-  W4A16_ERR_HIP = 5          /* a HIP runtime call failed */
+  W4A16_ERR_HIP = 5,         /* a HIP runtime call failed */
+  W4A16_ERR_NOALLOC_LIMIT = 6 /* the call needs more scratch than w4a16_moe_routed_forward_noalloc holds */
 } w4a16_status;
 
 /* Layer shape. group_size must be 32; hidden must be a multiple of 64 and
@@ -333,6 +335,29 @@ int w4a16_moe_routed_forward(const w4a16_moe_shape* shape, const uint16_t* x, in
                              int32_t num_experts_global, const int32_t* topk_ids, const float* topk_weights,
                              const void* w13_packed, const void* w2_packed, uint16_t* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture
+ * that must not allocate, tight serving loops, harnesses that forbid hipMalloc):
+ * w4a16_moe_routed_forward with its workspace in a static device array of
+ * W4A16_NOALLOC_SCRATCH_BYTES inside the library instead of a caller buffer.
+ * The caller still passes inputs and outputs, as for w4a16_moe_routed_forward.
+ *
+ * Ownership: each GPU the library runs on holds its own copy of the array from
+ * the first call on that GPU until the process ends; the call allocates and
+ * frees nothing. Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents: calls that overlap on one GPU (several streams, or
+ * several host threads with work in flight at once) race on it and must be
+ * serialised by the caller. Nothing needs the array cleared between calls.
+ * Errors: those of w4a16_moe_routed_forward, plus W4A16_ERR_NOALLOC_LIMIT when
+ * w4a16_moe_routed_workspace_bytes(shape, T, topk, num_experts_global) exceeds
+ * W4A16_NOALLOC_SCRATCH_BYTES (e.g. decode-sized calls of the Kimi-K2 expert
+ * slice fit: 128 tokens x top-8 over 48 of 384 experts need about 37 MiB), and
+ * W4A16_ERR_HIP when the array's address cannot be obtained. Bits of the
+ * output equal those of w4a16_moe_routed_forward on the same inputs. */
+#define W4A16_NOALLOC_SCRATCH_BYTES (64u << 20)
+int w4a16_moe_routed_forward_noalloc(const w4a16_moe_shape* shape, const uint16_t* x, int32_t T, int32_t topk,
+                                     int32_t num_experts_global, const int32_t* topk_ids, const float* topk_weights,
+                                     const void* w13_packed, const void* w2_packed, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Expert-grouped activation layouts                                         */

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert w.w4a16_status_string(code) not in ("", "unknown status")
     assert w.w4a16_status_string(99) == "unknown status"
 

@@ -15,7 +15,8 @@ __all__ = [
     "W4A16Error", "Shape", "LIB_PATH", "load", "make_shape", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "moe_align_capacity", "moe_align_workspace_bytes", "w4a16_choose_block_m", "moe_align",
     "moe_route_align", "moe_align_filtered", "moe_align_split", "w4a16_moe_routed_workspace_bytes", "w4a16_moe_routed_split",
-    "w4a16_moe_routed_forward", "w4a16_moe_contiguous_workspace_bytes", "w4a16_moe_contiguous_forward",
+    "w4a16_moe_routed_forward", "w4a16_moe_routed_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "w4a16_moe_contiguous_workspace_bytes", "w4a16_moe_contiguous_forward",
     "w4a16_moe_masked_block_m", "w4a16_moe_masked_workspace_bytes", "w4a16_moe_masked_forward",
     "w4a16_moe_stage_workspace_bytes", "w4a16_moe_prepare_x", "w4a16_moe_prepare_h",
     "w4a16_moe_workspace_bytes", "w4a16_moe_forward", "w4a16_moe_gate_up", "w4a16_moe_down",
@@ -162,6 +163,18 @@ def w4a16_moe_routed_forward(shape: Shape, x, topk_ids, topk_weights, num_expert
     _check(load().w4a16_moe_routed_forward(ctypes.byref(shape), _p(x), T, topk, num_experts_global, _p(topk_ids),
                                            _p(topk_weights), _p(w13_packed), _p(w2_packed), _p(out), _p(workspace),
                                            _nbytes(workspace), _stream(stream)), "w4a16_moe_routed_forward")
+
+
+# W4A16_NOALLOC_SCRATCH_BYTES of include/w4a16_moe.h
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w4a16_moe_routed_forward_noalloc(shape: Shape, x, topk_ids, topk_weights, num_experts_global: int, w13_packed,
+                                     w2_packed, out, stream=None):
+    T, topk = topk_ids.shape
+    _check(load().w4a16_moe_routed_forward_noalloc(ctypes.byref(shape), _p(x), T, topk, num_experts_global,
+                                                   _p(topk_ids), _p(topk_weights), _p(w13_packed), _p(w2_packed),
+                                                   _p(out), _stream(stream)), "w4a16_moe_routed_forward_noalloc")
 
 
 def w4a16_moe_workspace_bytes(shape: Shape, T: int, topk: int, block_m: int) -> int:

@@ -31,6 +31,7 @@ SIGNATURES = {
     "w4a16_moe_routed_workspace_bytes": (SZ, [P, I32, I32, I32]),
     "w4a16_moe_routed_split": (I32, [P, I32, I32, I32]),
     "w4a16_moe_routed_forward": (ctypes.c_int, [P, P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
+    "w4a16_moe_routed_forward_noalloc": (ctypes.c_int, [P, P, I32, I32, I32, P, P, P, P, P, P]),
     "moe_route_align": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P]),
     "w4a16_moe_contiguous_workspace_bytes": (SZ, [P, I32]),
     "w4a16_moe_contiguous_forward": (ctypes.c_int, [P, P, I32, P, P, P, P, P, SZ, P]),

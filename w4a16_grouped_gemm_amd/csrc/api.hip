@@ -89,6 +89,7 @@ const char* w4a16_status_string(int status) {
     case W4A16_ERR_CAPACITY: return "sorted_token_ids capacity too small";
     case W4A16_ERR_WORKSPACE: return "workspace too small";
     case W4A16_ERR_HIP: return "HIP runtime error";
+    case W4A16_ERR_NOALLOC_LIMIT: return "call needs more scratch than the no-alloc entry point's static array";
     default: return "unknown status";
   }
 }
