@@ -21,9 +21,9 @@
 //    mbcnt of its peers below it); one 16-lane DPP row scan per expert across
 //    the 16 waves gives the bases. Positions depend only on the input, never
 //    on timing;
-//  * each used block is labelled by a 16-lane group (one binary search), which
-//    also writes that block's padding sentinels; the unused tail is a plain
-//    fill: no per-position search over the over-allocated buffer;
+//  * each expert's thread labels its blocks and writes its padding sentinels
+//    (no search); the unused tail is a plain fill: no per-position search over
+//    the over-allocated buffer;
 //  * barriers order LDS traffic only; they never wait for global stores.
 // Small inputs run in one block and one launch. Larger ones use two launches:
 // per-chunk histograms, then one block per chunk that recomputes the (small)
@@ -42,8 +42,15 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPerThread = 8;                        // ids per thread held in registers
-constexpr int kChunk = kThreads * kPerThread;        // ids per block (8192)
-constexpr int kSmallMax = kChunk;                    // single-launch path up to here
+constexpr int kSmallMax = kThreads * kPerThread;     // single-launch paths up to here (8192)
+constexpr int kChunk = kThreads;                     // ids per block of the two-launch path
+// The scatter's per-wave counters are stored expert-major, wtab[e * kWtabStride +
+// wave]: the 16 waves' counters of one expert are consecutive (the per-expert
+// scan reads them as one conflict-free row), and the stride of 17 puts the
+// experts a wave's lanes touch in one ranking step on different LDS banks
+// (a wave-major table with a row stride of E = 384 put the scan's 16 lanes on
+// one bank).
+constexpr int kWtabStride = kWaves + 1;
 
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ int rank_below(uint64_t mask) {
@@ -161,39 +168,29 @@ __device__ void scan_offsets(int* counts, int E, int bm, int* off, int* cursor, 
   }
 }
 
-// Largest e in [0, E) with off[e] <= p (requires p < off[E]), found by the 16
-// lanes of a group (lanes 16 g .. 16 g + 15 of a wave, all active) together:
-// each step tests 16 evenly spaced candidates at once (E = 48: two steps; 512: three).
-__device__ __forceinline__ int find_expert16(const int* off, int E, int p, int sub) {
-  const int shift = (int)threadIdx.x & 48;  // this group's bits in the wave's ballot
-  int lo = 0, span = E;                     // off[lo] <= p; the answer lies in [lo, lo + span)
-  while (span > 1) {
-    const int step = (span + 15) >> 4;
-    const bool ok = sub * step < span && off[lo + sub * step] <= p;
-    const uint32_t bits = (uint32_t)(__ballot(ok) >> shift) & 0xffffu;  // bit 0 set: off[lo] <= p
-    const int k = 31 - __clz(bits);
-    lo += k * step;
-    span = min(step, span - k * step);
+// Block labels and padding sentinels from the experts' side: the 16-lane group
+// of expert e (experts g0, g0 + gstep, ...) writes expert_ids for e's blocks and
+// the sentinel into e's padding slots (only an expert's last block holds
+// padding, at most block_m - 1 slots), 16 at a time. An expert knows its own
+// blocks, so no block has to search for its expert (a per-block 16-way search
+// over the offsets cost 5.3 of 16.5 us for 4096 ids over 384 experts).
+__device__ void label_experts(const int* off, const int* counts, int E, int bm, int32_t* sorted, int32_t* expert_ids,
+                              int nblk, int capacity, int sentinel, int g0, int gstep) {
+  const int sub = (int)threadIdx.x & 15;
+  for (int e = g0; e < E; e += gstep) {
+    const int c = counts[e];
+    if (c == 0) continue;
+    const int end = off[e] + padded(c, bm);
+    for (int b = off[e] / bm + sub; b < min(end / bm, nblk); b += 16) expert_ids[b] = e;
+    for (int p = off[e] + c + sub; p < min(end, capacity); p += 16) sorted[p] = sentinel;
   }
-  return lo;
 }
 
-// Block labels and padding sentinels, one 16-lane group per used block b
-// (groups g0, g0 + gstep, ...): the group finds b's expert by a 16-way search,
-// its lane 0 labels the
-// block and its lanes fill the block's padding slots. Only an expert's last
-// block holds padding (at most block_m - 1 slots).
-__device__ void label_blocks(const int* off, const int* counts, int E, int bm, int32_t* sorted, int32_t* expert_ids,
-                             int nblk, int capacity, int sentinel, int g0, int gstep) {
-  const int used = min(off[E] / bm, nblk);  // == off[E] / bm: capacity covers every padded count
-  const int sub = (int)threadIdx.x & 15;
-  for (int b = g0; b < used; b += gstep) {
-    const int e = find_expert16(off, E, b * bm, sub);
-    if (sub == 0) expert_ids[b] = e;
-    const int end = min((b + 1) * bm, capacity);
-    for (int p = max(b * bm, off[e] + counts[e]) + sub; p < end; p += 16) sorted[p] = sentinel;
-  }
-}
+// Expert groups of a launch, interleaved over its blocks so that every block
+// (compute unit) takes a share of the label stores: group (thread / 16) of
+// block b is global group (thread / 16) * gridDim + b.
+__device__ __forceinline__ int expert_group0() { return ((int)threadIdx.x >> 4) * (int)gridDim.x + (int)blockIdx.x; }
+__device__ __forceinline__ int expert_gstep() { return (kThreads / 16) * (int)gridDim.x; }
 
 // Unused tail: sorted[ntpp, capacity) = sentinel, expert_ids[ntpp / bm, nblk) = -1.
 __device__ void fill_tail(int ntpp, int bm, int32_t* sorted, int capacity, int32_t* expert_ids, int nblk,
@@ -204,16 +201,16 @@ __device__ void fill_tail(int ntpp, int bm, int32_t* sorted, int capacity, int32
 
 // Stable scatter of the block's ids (held in v, see id_index): the id at flat
 // index i goes to cursor[e] + (resident ids of e before i in this block).
-// Each wave ranks its own contiguous segment step by step against a
-// wave-private counter row wcnt[wave][e] in LDS (lanes of one expert in a step
+// Each wave ranks its own contiguous segment step by step against its own
+// counters wcnt[e * kWtabStride + wave] in LDS (lanes of one expert in a step
 // are found with one ballot per id bit; the rank is the mbcnt of the peers
 // below), so the steps need no workgroup barrier. The 16 per-wave counts of an
 // expert are then turned into per-wave bases by one 16-lane row scan. wcnt is
-// LDS scratch of kWaves * E ints, zeroed by the caller before its last barrier.
+// LDS scratch of kWtabStride * E ints, zeroed by the caller before its last barrier.
 __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nbits, const int* counts,
                             const int* cursor, int* wcnt, int32_t* __restrict__ sorted, int capacity, int lo) {
   const int wave = (int)threadIdx.x >> 6;
-  int* row = wcnt + wave * E;
+  int* row = wcnt + wave;  // this wave's counter of expert e: row[e * kWtabStride]
   int rank[kPerThread];
 #pragma unroll
   for (int r = 0; r < kPerThread; ++r) {
@@ -228,31 +225,32 @@ __device__ void scatter_ids(const int (&v)[kPerThread], int steps, int E, int nb
         peers &= bit ? m : ~m;
       }
       const int below = rank_below(peers);
-      const int prev = local ? row[e] : 0;  // every lane reads before the leader writes
+      const int prev = local ? row[e * kWtabStride] : 0;  // every lane reads before the leader writes
       rank[r] = prev + below;
-      if (local && below == 0) row[e] = prev + __popcll(peers);
+      if (local && below == 0) row[e * kWtabStride] = prev + __popcll(peers);
     }
   }
   lds_barrier();  // all waves' counts final
-  // pair (expert x, wave w) at index 16 x + w: one 16-lane row holds one expert;
-  // kWaves * E is a multiple of 16, so every row is fully active
+  // pair (expert x, wave w) at thread index 16 x + w: one 16-lane row holds one
+  // expert's consecutive counters; kWaves * E is a multiple of 16, so every row
+  // is fully active
   for (int idx = (int)threadIdx.x; idx < kWaves * E; idx += kThreads) {
     const int x = idx >> 4, w = idx & 15;
-    const int c = wcnt[w * E + x];
-    wcnt[w * E + x] = cursor[x] + row_incl_scan(c) - c;  // only this lane ever touches this entry
+    const int c = wcnt[x * kWtabStride + w];
+    wcnt[x * kWtabStride + w] = cursor[x] + row_incl_scan(c) - c;  // only this lane ever touches this entry
   }
   lds_barrier();  // per-wave bases visible
 #pragma unroll
   for (int r = 0; r < kPerThread; ++r)
     if (r < steps && (unsigned)v[r] < (unsigned)E && counts[v[r]] > 0) {
-      const int pos = row[v[r]] + rank[r];  // < capacity: the capacity covers every padded count
+      const int pos = row[v[r] * kWtabStride] + rank[r];  // < capacity: the capacity covers every padded count
       if ((unsigned)pos < (unsigned)capacity) sorted[pos] = id_index(lo, steps, r);
     }
 }
 
 // ---- single-launch path -----------------------------------------------------
 // The whole alignment of n <= kSmallMax ids held in v (see id_index, lo = 0) by
-// one block. LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
+// one block. LDS: counts[E], off[E+1], cursor[E], wtab[kWtabStride*E]
 __device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, int* smem, int32_t* __restrict__ sorted,
                             int capacity, int32_t* __restrict__ expert_ids, int nblk, int32_t* __restrict__ ntpp_out,
                             int32_t* __restrict__ counts_out, CountRange keep) {
@@ -262,15 +260,14 @@ __device__ void align_block(const int (&v)[kPerThread], int n, int E, int bm, in
   int* wtab = cursor + E;
   const int steps = block_steps(0, n);
   for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = 0;
-  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
+  for (int k = (int)threadIdx.x; k < kWtabStride * E; k += kThreads) wtab[k] = 0;
   lds_barrier();
   count_ids(v, E, counts);
   lds_barrier();
   scan_offsets(counts, E, bm, off, cursor, false, counts_out, ntpp_out, keep);
   lds_barrier();
   const int ntpp = off[E];
-  label_blocks(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, (int)threadIdx.x >> 4,
-               kThreads / 16);
+  label_experts(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, expert_group0(), expert_gstep());
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, (int)threadIdx.x, kThreads);
   lds_barrier();
   scatter_ids(v, steps, E, id_bits(E), counts, cursor, wtab, sorted, capacity, 0);
@@ -339,6 +336,57 @@ __global__ __launch_bounds__(kThreads) void align_small_kernel(const int32_t* __
   align_block(v, n, E, bm, smem, sorted, capacity, expert_ids, nblk, ntpp_out, counts_out, keep);
 }
 
+// ---- one launch, several blocks ----------------------------------------------
+// n ids in (kWaveMax, kSmallMax]: block b scatters the ids [b kSpread, (b+1)
+// kSpread) (one per thread) and labels its share of the experts; every block
+// counts all n ids itself (they are few and L2-resident after the first block
+// reads them), along with the ids of each expert before its own chunk, so no
+// block waits for another and there is no separate histogram launch. The
+// alignment's stores, mostly scattered 4-byte writes, then leave through
+// several compute units' memory pipelines instead of one (one block took
+// 13.6 us for 4096 ids over 384 experts, most of it in its stores).
+// LDS: counts[E], off[E+1], cursor[E], wtab[kWtabStride*E]
+constexpr int kSpread = kThreads;
+
+__global__ __launch_bounds__(kThreads) void align_spread_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
+                                                                int32_t* __restrict__ sorted, int capacity,
+                                                                int32_t* __restrict__ expert_ids, int nblk,
+                                                                int32_t* __restrict__ ntpp_out,
+                                                                int32_t* __restrict__ counts_out, CountRange keep) {
+  extern __shared__ int smem[];
+  int* counts = smem;
+  int* off = counts + E;
+  int* cursor = off + E + 1;
+  int* wtab = cursor + E;
+  const int lo = (int)blockIdx.x * kSpread;
+  const int hi = min(n, lo + kSpread);
+  int v[kPerThread];
+  load_ids(ids, lo, hi, 1, v);
+  for (int e = (int)threadIdx.x; e < E; e += kThreads) counts[e] = cursor[e] = 0;
+  for (int k = (int)threadIdx.x; k < kWtabStride * E; k += kThreads) wtab[k] = 0;
+  lds_barrier();
+  // every id, and the ids before this chunk (into cursor: this chunk's base
+  // inside each expert); all loads are issued before the first count
+  const int steps = block_steps(0, n);
+  int va[kPerThread];
+  load_ids(ids, 0, n, steps, va);
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r)
+    if ((unsigned)va[r] < (unsigned)E) {
+      atomicAdd(&counts[va[r]], 1);
+      if (id_index(0, steps, r) < lo) atomicAdd(&cursor[va[r]], 1);
+    }
+  lds_barrier();
+  const bool first = blockIdx.x == 0;
+  scan_offsets(counts, E, bm, off, cursor, true, first ? counts_out : nullptr, first ? ntpp_out : nullptr, keep);
+  lds_barrier();
+  const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
+  label_experts(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, expert_group0(), expert_gstep());
+  fill_tail(off[E], bm, sorted, capacity, expert_ids, nblk, n, gt, gstep);
+  lds_barrier();
+  scatter_ids(v, 1, E, id_bits(E), counts, cursor, wtab, sorted, capacity, lo);
+}
+
 // ---- multi-block path -------------------------------------------------------
 // Workspace: hist[nchunks * E], the per-chunk resident counts.
 __global__ __launch_bounds__(kThreads) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E,
@@ -354,11 +402,38 @@ __global__ __launch_bounds__(kThreads) void align_hist_kernel(const int32_t* __r
   for (int e = (int)threadIdx.x; e < E; e += kThreads) hist[(size_t)blockIdx.x * E + e] = smem[e];
 }
 
+// Expert totals and this block's base inside each expert from the per-chunk
+// histograms: a wave per expert, its lanes reading the chunks' counts in
+// parallel (L2 hits), then wave-wide sums; written to total/before and, when
+// given, their copies total2/before2.
+__device__ void chunk_sums(const int* __restrict__ hist, int nchunks, int E, int* total, int* before,
+                           int* total2 = nullptr, int* before2 = nullptr) {
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  for (int e = wave; e < E; e += kWaves) {  // uniform per wave: every lane takes part in the sums
+    int t = 0, b = 0;
+    for (int k = lane; k < nchunks; k += 64) {
+      const int c = hist[(size_t)k * E + e];
+      t += c;
+      b += k < (int)blockIdx.x ? c : 0;
+    }
+    t = __builtin_amdgcn_readlane(wave_incl_scan(t), 63);
+    b = __builtin_amdgcn_readlane(wave_incl_scan(b), 63);
+    if (lane == 0) {
+      total[e] = t;
+      before[e] = b;
+      if (total2) {
+        total2[e] = t;
+        before2[e] = b;
+      }
+    }
+  }
+}
+
 // One block per chunk. Every block reads all chunk histograms (nchunks * E
 // entries) to get the expert totals, the offsets and its own chunk's base;
 // block 0 also writes the counts, the padded total and the block labels; all
 // blocks share the sentinel fill of the tail.
-// LDS: counts[E], off[E+1], cursor[E], wtab[kWaves*E]
+// LDS: counts[E], off[E+1], cursor[E], wtab[kWtabStride*E]
 __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int bm,
                                                                  const int* __restrict__ hist, int nchunks,
                                                                  int32_t* __restrict__ sorted, int capacity,
@@ -374,25 +449,15 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
   const int lo = (int)blockIdx.x * kChunk;
   const int steps = block_steps(lo, min(n, lo + kChunk));
   load_ids(ids, lo, min(n, lo + kChunk), steps, v);
-  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
-    int total = 0, before = 0;
-#pragma unroll 8  // independent loads in flight (the histograms sit in L2)
-    for (int b = 0; b < nchunks; ++b) {
-      const int c = hist[(size_t)b * E + e];
-      before += (b < (int)blockIdx.x) ? c : 0;
-      total += c;
-    }
-    counts[e] = total;
-    cursor[e] = before;  // this chunk's base inside the expert, before adding off[e]
-  }
+  for (int k = (int)threadIdx.x; k < kWtabStride * E; k += kThreads) wtab[k] = 0;
+  chunk_sums(hist, nchunks, E, counts, cursor);  // cursor: this chunk's base inside each expert, before off[e]
   lds_barrier();
   scan_offsets(counts, E, bm, off, cursor, true, blockIdx.x == 0 ? counts_out : nullptr,
                blockIdx.x == 0 ? ntpp_out : nullptr, keep);
   lds_barrier();
   const int ntpp = off[E];
   const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
-  label_blocks(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, gt >> 4, gstep / 16);
+  label_experts(off, counts, E, bm, sorted, expert_ids, nblk, capacity, n, expert_group0(), expert_gstep());
   fill_tail(ntpp, bm, sorted, capacity, expert_ids, nblk, n, gt, gstep);
   lds_barrier();
   scatter_ids(v, steps, E, id_bits(E), counts, cursor, wtab, sorted, capacity, lo);
@@ -404,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
 // that count range. Set 1's sorted array directly follows set 0's (sorted +
 // cap0), so one stable scatter into the joined array serves both: an expert of
 // set 1 starts its cursor at cap0 + its offset in set 1.
-// LDS: cnt0[E], off0[E+1], cur0[E], wtab[kWaves*E], cnt1[E], off1[E+1],
+// LDS: cnt0[E], off0[E+1], cur0[E], wtab[kWtabStride*E], cnt1[E], off1[E+1],
 // cur1[E], kept[E]
 __global__ __launch_bounds__(kThreads) void align_scatter2_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                                   int split, const int* __restrict__ hist, int nchunks,
@@ -418,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter2_kernel(const int32_t*
   int* off0 = cnt0 + E;
   int* cur0 = off0 + E + 1;
   int* wtab = cur0 + E;
-  int* cnt1 = wtab + kWaves * E;
+  int* cnt1 = wtab + kWtabStride * E;
   int* off1 = cnt1 + E;
   int* cur1 = off1 + E + 1;
   int* kept = cur1 + E;
@@ -426,18 +491,8 @@ __global__ __launch_bounds__(kThreads) void align_scatter2_kernel(const int32_t*
   const int lo = (int)blockIdx.x * kChunk;
   const int steps = block_steps(lo, min(n, lo + kChunk));
   load_ids(ids, lo, min(n, lo + kChunk), steps, v);
-  for (int k = (int)threadIdx.x; k < kWaves * E; k += kThreads) wtab[k] = 0;
-  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
-    int total = 0, before = 0;
-#pragma unroll 8
-    for (int b = 0; b < nchunks; ++b) {
-      const int c = hist[(size_t)b * E + e];
-      before += (b < (int)blockIdx.x) ? c : 0;
-      total += c;
-    }
-    cnt0[e] = cnt1[e] = total;
-    cur0[e] = cur1[e] = before;
-  }
+  for (int k = (int)threadIdx.x; k < kWtabStride * E; k += kThreads) wtab[k] = 0;
+  chunk_sums(hist, nchunks, E, cnt0, cur0, cnt1, cur1);
   lds_barrier();
   const bool first = blockIdx.x == 0;
   // both scans run on wave 0, one after the other (its LDS accesses stay in order)
@@ -445,8 +500,8 @@ __global__ __launch_bounds__(kThreads) void align_scatter2_kernel(const int32_t*
   scan_offsets(cnt1, E, bm1, off1, cur1, true, nullptr, first ? ntpp1 : nullptr, CountRange{1, split - 1});
   lds_barrier();
   const int gt = (int)(blockIdx.x * kThreads + threadIdx.x), gstep = (int)(gridDim.x * kThreads);
-  label_blocks(off0, cnt0, E, bm0, sorted, eids0, nblk0, cap0, n, gt >> 4, gstep / 16);
-  label_blocks(off1, cnt1, E, bm1, sorted + cap0, eids1, nblk1, cap1, n, gt >> 4, gstep / 16);
+  label_experts(off0, cnt0, E, bm0, sorted, eids0, nblk0, cap0, n, expert_group0(), expert_gstep());
+  label_experts(off1, cnt1, E, bm1, sorted + cap0, eids1, nblk1, cap1, n, expert_group0(), expert_gstep());
   fill_tail(off0[E], bm0, sorted, cap0, eids0, nblk0, n, gt, gstep);
   fill_tail(off1[E], bm1, sorted + cap0, cap1, eids1, nblk1, n, gt, gstep);
   // joined view: kept[e] = the expert's count in whichever set holds it (the
@@ -649,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void route_align_small_kernel(
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-size_t scatter_lds(int E) { return sizeof(int) * (size_t)(3 * E + 1 + kWaves * E); }
+size_t scatter_lds(int E) { return sizeof(int) * (size_t)(3 * E + 1 + kWtabStride * E); }
 // align_scatter2_kernel: the one-set layout, then cnt1[E], off1[E+1], cur1[E], kept[E]
 size_t scatter2_lds(int E) { return scatter_lds(E) + sizeof(int) * (size_t)(4 * E + 1); }
 
@@ -672,9 +727,14 @@ hipError_t launch_align(const int32_t* ids, int32_t n, int32_t E, int32_t bm, in
                        ntpp, counts, E);
     return hipGetLastError();
   }
-  if (n <= kSmallMax) {
+  if (n <= kSpread) {  // one block: the whole alignment (one wave up to 64 ids)
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kThreads), scatter_lds(E), stream, ids, n, E, bm, sorted,
                        capacity, expert_ids, nblk, ntpp, counts, keep);
+    return hipGetLastError();
+  }
+  if (n <= kSmallMax) {
+    hipLaunchKernelGGL(align_spread_kernel, dim3((n + kSpread - 1) / kSpread), dim3(kThreads), scatter_lds(E), stream,
+                       ids, n, E, bm, sorted, capacity, expert_ids, nblk, ntpp, counts, keep);
     return hipGetLastError();
   }
   const int nchunks = (n + kChunk - 1) / kChunk;
