@@ -30,19 +30,24 @@
 // such tiny elements in h routinely; they cannot move a result that the fp32
 // sum resolves.
 //
-// Tile: a 512-thread workgroup (8 waves) computes 128 rows x 256 channels (four
+// Tile: a 256-thread workgroup (4 waves) computes 128 rows x 256 channels (four
 // 64-channel n-blocks) over the whole reduction. Wave w owns all 128 rows and
-// two 16-channel column blocks of n-block w / 2: blocks (w & 1) and (w & 1) + 2,
-// i.e. matching gate and up channels for the gate_up projection. Each weight is
-// dequantised by exactly one wave. The K loop moves in stages of two groups:
-//   A  128 rows x 64 k of fp16 (16 KiB), gathered through sorted_token_ids,
-//   B  4 n-blocks x 2 groups of packed nibbles (8 KiB) and fp16 scales (1 KiB),
+// the four 16-channel column blocks of n-block w (for gate_up: gate channels in
+// blocks 0, 1 and the matching up channels in 2, 3), so each weight is
+// dequantised by exactly one wave and feeds 8 row blocks of MFMAs, and each A
+// fragment read from LDS feeds 4 MFMAs. The K loop moves in stages of two groups:
+//   A  128 rows x 64 k of fp16 (16 KiB), gathered through sorted_token_ids and
+//      shared by the four waves,
+//   B  per wave, its own n-block's 2 groups of packed nibbles (2 KiB) and fp16
+//      scales (256 B),
 // copied global -> LDS by global_load_lds_dwordx4 / _dword (no VGPRs in flight)
 // into a ring of kStages stages. LDS A is fragment-major (row block, group,
 // lane, 16 bytes): every MFMA operand is one conflict-free ds_read_b128. The
-// in-order vmcnt tracks the copies: a wave waits for its own copies of the
-// stage it is about to use, then a workgroup barrier makes every wave's copies
-// visible; the same barrier proves the slot refilled next has been consumed.
+// in-order vmcnt tracks the copies. A wave's weights are its own copies, so it
+// reads and dequantises the next stage's first group as soon as its own copies
+// of that stage landed, under the current stage's second group of MFMAs; the A
+// fragments need every wave's copies, published by one workgroup barrier per
+// stage, which also proves the slot refilled next has been consumed.
 //
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8, and the tiles an
 // XCD runs are the n-tiles of the row blocks mb = xcd (mod 8), so a row block's
@@ -61,17 +66,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kStages = 3;           // LDS ring depth
 constexpr int kTileM = 128;
 constexpr int kRowBlocks = kTileM / 16;
-constexpr int kTileNBlocks = 4;      // 4 x 64 = 256 channels
-constexpr int kStageGroups = 2;      // 64 k per stage
+constexpr int kTileNBlocks = kWaves;  // 4 x 64 = 256 channels, one n-block per wave
+constexpr int kStageGroups = 2;       // 64 k per stage
 constexpr int kABytes = kTileM * kStageGroups * kGroup * 2;                  // 16 KiB
-constexpr int kBBytes = kTileNBlocks * kStageGroups * kNibUnitBytes;         // 8 KiB
-constexpr int kSBytes = kTileNBlocks * kStageGroups * kScaleUnitElems * 2;   // 1 KiB
-constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
-constexpr int kCopiesPerWaveStage = 4;  // 2 A blocks + 1 nibble unit + 1 scale unit
+constexpr int kBWaveBytes = kStageGroups * kNibUnitBytes;                    // 2 KiB
+constexpr int kSWaveBytes = kStageGroups * kScaleUnitElems * 2;              // 256 B
+constexpr int kBOffset = kABytes;
+constexpr int kSOffset = kABytes + kWaves * kBWaveBytes;
+constexpr int kStageBytes = kSOffset + kWaves * kSWaveBytes;                 // 25 KiB
+constexpr int kABlocksPerWave = kRowBlocks / kWaves;                         // row blocks a wave copies
+// copies per wave and stage: its A row blocks x groups, its nibbles (one per
+// group) and its scales (both groups in one)
+constexpr int kCopiesPerWaveStage = kABlocksPerWave * kStageGroups + kStageGroups + 1;
 // A fragments read ahead of the MFMAs that use them
 constexpr int kAhead = 4;
 // Weights and scales are read once per tile: copied with the non-temporal
@@ -183,146 +194,187 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 struct TileCtx {
-  const uint8_t* a_src;  // this lane's A copy source (row start + 16-byte k offset)
-  const uint8_t* wq;     // nibble units of this wave's copy n-block, group 0
-  const uint8_t* ws;     // fp16 scale units of this wave's copy n-block, group 0
-  int copy_nb, copy_j;   // nibble / scale unit this wave copies: n-block, group in stage
+  const uint8_t* a_src[kABlocksPerWave];  // this lane's A copy sources (row start + 16-byte k offset)
+  const uint8_t* wq;                      // this wave's n-block: nibble units from group 0, + 16 lane
+  const uint8_t* ws;                      // this wave's n-block: fp16 scale units from group 0, + 4 lane
 };
 
-// Issue this wave's copies of stage `s` (groups 2s, 2s+1) into ring slot `slot`.
-__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int slot, int s, int wave, int lane) {
+// Issue this wave's copies of stage `s` (groups 2s, 2s+1) into ring slot `slot`:
+// its own nibbles and scales, then its share of the A row blocks.
+__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int slot, int s, int wave) {
   uint8_t* base = ring + slot * kStageBytes;
   const int g0 = s * kStageGroups;
 #pragma unroll
-  for (int j = 0; j < kStageGroups; ++j) {
-    const uint8_t* src = c.a_src + (int64_t)(g0 + j) * (kGroup * 2);
-    __builtin_amdgcn_global_load_lds(src, LDS_PTR(base + (wave * kStageGroups + j) * 1024), 16, 0, 0);
-  }
-  {
-    const uint8_t* src = c.wq + (int64_t)(g0 + c.copy_j) * kNibUnitBytes + 16 * lane;
-    __builtin_amdgcn_global_load_lds(src, LDS_PTR(base + kABytes + (c.copy_nb * kStageGroups + c.copy_j) * 1024), 16,
-                                     0, kNonTemporal);
-  }
-  // 128 bytes of scales: a dword copy lands at LDS base + 4 * lane, so only
-  // lanes 0..31 take part (one instruction per wave either way, which keeps
-  // every wave's count of pending copies the same)
-  if (lane < 32) {
-    const uint8_t* src = c.ws + (int64_t)(g0 + c.copy_j) * (kScaleUnitElems * 2) + 4 * lane;
-    __builtin_amdgcn_global_load_lds(
-        src, LDS_PTR(base + kABytes + kBBytes + (c.copy_nb * kStageGroups + c.copy_j) * 128), 4, 0, kNonTemporal);
-  }
+  for (int j = 0; j < kStageGroups; ++j)
+    __builtin_amdgcn_global_load_lds(c.wq + (int64_t)(g0 + j) * kNibUnitBytes,
+                                     LDS_PTR(base + kBOffset + wave * kBWaveBytes + j * kNibUnitBytes), 16, 0,
+                                     kNonTemporal);
+  // the two groups' scale units are adjacent: 64 lanes x 4 bytes cover both
+  __builtin_amdgcn_global_load_lds(c.ws + (int64_t)g0 * (kScaleUnitElems * 2),
+                                   LDS_PTR(base + kSOffset + wave * kSWaveBytes), 4, 0, kNonTemporal);
+#pragma unroll
+  for (int t = 0; t < kABlocksPerWave; ++t)
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+      const int rb = kABlocksPerWave * wave + t;
+      __builtin_amdgcn_global_load_lds(c.a_src[t] + (int64_t)(g0 + j) * (kGroup * 2),
+                                       LDS_PTR(base + (rb * kStageGroups + j) * 1024), 16, 0, 0);
+    }
 }
 
-// The K loop and epilogue of one tile for a wave owning column blocks HALF and
-// HALF + 2 of n-block wn (HALF is wave-uniform, so it is a template argument:
-// no per-group selects).
-template <int MODE, int HALF>
+// The K loop and epilogue of one tile for the wave owning n-block nt * 4 + wave.
+template <int MODE>
 __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c, uint8_t* ring, int nstages, int mb,
                                           int nt, int e, int wave, int lane) {
-  const int wn = wave >> 1;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   uint32_t magic = kF16_1024;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
-  floatx4 acc[kRowBlocks][2];
+  floatx4 acc[kRowBlocks][4];
 #pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) acc[rb][0] = acc[rb][1] = zero4;
+  for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = zero4;
+
+  // this wave's own weights of a stage: group j's 16 bytes of nibbles and the
+  // four scales of its column (entry 4 * (lane & 15) + cb of the unit)
+  const auto nib_of = [&](int slot, int j) {
+    return *reinterpret_cast<const u32x4*>(ring + slot * kStageBytes + kBOffset + wave * kBWaveBytes +
+                                           j * kNibUnitBytes + 16 * lane);
+  };
+  const auto sc_of = [&](int slot, int j) {
+    return *reinterpret_cast<const u32x2*>(ring + slot * kStageBytes + kSOffset + wave * kSWaveBytes +
+                                           j * (kScaleUnitElems * 2) + 8 * (lane & 15));
+  };
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const auto deq = [&](const u32x4& nib, const u32x2& sc, int cb) {
+    const uint32_t sbits = (cb & 2) ? sc.y : sc.x;
+    const f16x2 s2 = splat((cb & 1) ? sbits >> 16 : sbits & 0xFFFFu);
+    return dequant(nib[cb], s2, s2 * sixteenth, magic);
+  };
 
   // the previous tile's reads of every slot are done before it is refilled
   ring_barrier();
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < nstages) issue_stage(c, ring, s, s, wave, lane);
+    if (s < nstages) issue_stage(c, ring, s, s, wave);
+
+  // stage 0's first group, dequantised before the loop, and its second
+  // group's nibbles and scales (own copies only)
+  if (1 < nstages) wait_vmcnt<kCopiesPerWaveStage>();
+  else wait_vmcnt<0>();
+  f16x8 w[4];
+  u32x4 nib1 = nib_of(0, 1);
+  u32x2 sc1 = sc_of(0, 1);
+  {
+    const u32x4 nb = nib_of(0, 0);
+    const u32x2 sc = sc_of(0, 0);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) w[cb] = deq(nb, sc, cb);
+  }
 
   for (int s = 0; s < nstages; ++s) {
-    // own copies of stage s landed (later stages may still be in flight) ...
-    if (s + kStages - 2 < nstages) wait_vmcnt<(kStages - 2) * kCopiesPerWaveStage>();
-    else wait_vmcnt<0>();
-    // ... and everyone's; everyone also finished reading stage s - 1
+    const int slot = s % kStages;
+    // every wave waited for its own copies of stage s before this barrier;
+    // everyone also finished reading stage s - 1, whose slot is refilled here
     ring_barrier();
-    if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave, lane);
+    if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave);
 
     // Software pipeline inside the stage: while a group's MFMAs run, the wave
-    // reads the A fragments kAhead row blocks ahead (wrapping into the next
-    // group) and dequantises the next group's weights; each MFMA pair sits in
-    // its own scheduling region so the compiler keeps that interleave.
-    const uint8_t* base = ring + (s % kStages) * kStageBytes;
+    // reads the A fragments kAhead row blocks ahead and dequantises the next
+    // group's weights (for the second group: the next stage's first group);
+    // each row block's MFMAs sit in their own scheduling region so the
+    // compiler keeps that interleave.
+    const uint8_t* abase = ring + slot * kStageBytes;
     const auto lds_a = [&](int rb, int j) {
       return __builtin_bit_cast(f16x8,
-                                *reinterpret_cast<const u32x4*>(base + (rb * kStageGroups + j) * 1024 + 16 * lane));
-    };
-    u32x4 nib[kStageGroups];
-    u32x2 sc[kStageGroups];
-#pragma unroll
-    for (int j = 0; j < kStageGroups; ++j) {
-      nib[j] = *reinterpret_cast<const u32x4*>(base + kABytes + (wn * kStageGroups + j) * 1024 + 16 * lane);
-      // entry 4 * (lane & 15) + c of the unit is column block c's scale
-      sc[j] = *reinterpret_cast<const u32x2*>(base + kABytes + kBBytes + (wn * kStageGroups + j) * 128 +
-                                             8 * (lane & 15));
-    }
-    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const auto deq0 = [&](int j) {
-      const f16x2 s2 = splat(HALF ? sc[j].x >> 16 : sc[j].x & 0xFFFFu);
-      return dequant(HALF ? nib[j].y : nib[j].x, s2, s2 * sixteenth, magic);
-    };
-    const auto deq1 = [&](int j) {
-      const f16x2 s2 = splat(HALF ? sc[j].y >> 16 : sc[j].y & 0xFFFFu);
-      return dequant(HALF ? nib[j].w : nib[j].z, s2, s2 * sixteenth, magic);
+                                *reinterpret_cast<const u32x4*>(abase + (rb * kStageGroups + j) * 1024 + 16 * lane));
     };
     f16x8 a[kRowBlocks];
 #pragma unroll
     for (int rb = 0; rb < kAhead; ++rb) a[rb] = lds_a(rb, 0);
-    f16x8 w0 = deq0(0), w1 = deq1(0);
-#pragma unroll
-    for (int j = 0; j < kStageGroups; ++j) {
-      f16x8 v0 = w0, v1 = w1;
+    {
+      const u32x4 nb = nib1;
+      const u32x2 sc = sc1;
+      f16x8 v[4];
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
         __builtin_amdgcn_sched_barrier(0);
-        acc[rb][0] = mfma16(a[rb], w0, acc[rb][0]);
-        acc[rb][1] = mfma16(a[rb], w1, acc[rb][1]);
-        if (rb + kAhead < kRowBlocks) a[rb + kAhead] = lds_a(rb + kAhead, j);
-        else if (j + 1 < kStageGroups) a[rb + kAhead - kRowBlocks] = lds_a(rb + kAhead - kRowBlocks, j + 1);
-        if (j + 1 < kStageGroups && rb == 1) v0 = deq0(j + 1);
-        if (j + 1 < kStageGroups && rb == 3) v1 = deq1(j + 1);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(a[rb], w[cb], acc[rb][cb]);
+        if (rb + kAhead < kRowBlocks) a[rb + kAhead] = lds_a(rb + kAhead, 0);
+        else a[rb + kAhead - kRowBlocks] = lds_a(rb + kAhead - kRowBlocks, 1);
+        if (rb >= 1 && rb <= 4) v[rb - 1] = deq(nb, sc, rb - 1);
       }
-      w0 = v0;
-      w1 = v1;
+      // keep the dequantisation here, under these MFMAs: without a use in this
+      // block the compiler sinks it past the wait below, into the next group
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        asm volatile("" : "+v"(v[cb]));
+        w[cb] = v[cb];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // own copies of stage s + 1 landed (stage s + 2 may still be in flight);
+    // after the last stage the reads below see a stale slot whose values are unused
+    if (s + 2 < nstages) wait_vmcnt<kCopiesPerWaveStage>();
+    else wait_vmcnt<0>();
+    {
+      // the next stage's weights: the first group is dequantised under this
+      // group's MFMAs, the second is read now for the next stage's first group
+      const int nslot = (s + 1) % kStages;
+      const u32x4 nb = nib_of(nslot, 0);
+      const u32x2 sc = sc_of(nslot, 0);
+      nib1 = nib_of(nslot, 1);
+      sc1 = sc_of(nslot, 1);
+      f16x8 v[4];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(a[rb], w[cb], acc[rb][cb]);
+        if (rb + kAhead < kRowBlocks) a[rb + kAhead] = lds_a(rb + kAhead, 1);
+        if (rb >= 1 && rb <= 4) v[rb - 1] = deq(nb, sc, rb - 1);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) w[cb] = v[cb];
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue: rows 16 rb + 4 (lane >> 4) + i of the tile; packed channels
-  // 64 nb + 16 c + (lane & 15) for c = HALF, HALF + 2.
-  const int nb = nt * kTileNBlocks + wn;
-  const int pc0 = nb * kNBlock + 16 * HALF + (lane & 15);
+  // 64 nb + 16 cb + (lane & 15).
+  const int nb = nt * kTileNBlocks + wave;
+  const int pc0 = nb * kNBlock + (lane & 15);
   const int32_t* cexp = p.col_exp + (int64_t)e * p.N;
-  const int ce0 = cexp[pc0], ce1 = cexp[pc0 + 32];
+  int ce[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) ce[cb] = cexp[pc0 + 16 * cb];
+  const int q = lane & 3;
   if (MODE == kDown && !p.out_bf16) {
     // fp32 rows of y: a 4 x 4 transpose inside each lane quad turns a lane's
     // four rows of one channel into one row of four consecutive channels, so
     // each lane stores 16 bytes per row block and column block (a quarter of
     // the store instructions of one float per row)
-    const int q = lane & 3;
-    float* ybase = static_cast<float*>(p.out) + nb * kNBlock + 16 * HALF + 4 * ((lane & 15) >> 2);
+    float* ybase = static_cast<float*>(p.out) + nb * kNBlock + 4 * ((lane & 15) >> 2);
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      float v0[4], v1[4];
-      int ids[4];
+      int ids[4], re[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + i;
         ids[i] = p.sorted[prow];
-        const int re = p.row_exp[prow];  // padding rows: any value, never stored
-        v0[i] = __builtin_amdgcn_ldexpf(acc[rb][0][i], re + ce0);
-        v1[i] = __builtin_amdgcn_ldexpf(acc[rb][1][i], re + ce1);
+        re[i] = p.row_exp[prow];  // padding rows: any value, never stored
       }
-      quad_transpose(v0, lane);
-      quad_transpose(v1, lane);
       const int id = q == 0 ? ids[0] : q == 1 ? ids[1] : q == 2 ? ids[2] : ids[3];
-      if ((unsigned)id < (unsigned)p.n_slots) {
-        float* y = ybase + (int64_t)id * p.out_ld;
-        *reinterpret_cast<floatx4*>(y) = floatx4{v0[0], v0[1], v0[2], v0[3]};
-        *reinterpret_cast<floatx4*>(y + 32) = floatx4{v1[0], v1[1], v1[2], v1[3]};
+      float* y = ybase + (int64_t)id * p.out_ld;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_ldexpf(acc[rb][cb][i], re[i] + ce[cb]);
+        quad_transpose(v, lane);
+        if ((unsigned)id < (unsigned)p.n_slots)
+          *reinterpret_cast<floatx4*>(y + 16 * cb) = floatx4{v[0], v[1], v[2], v[3]};
       }
     }
     return;
@@ -331,31 +383,36 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     // h rows: the same quad transpose, four consecutive bf16 channels of one
     // row per lane in one 8-byte store
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const int q = lane & 3;
-    __bf16* hbase = static_cast<__bf16*>(p.out) + nb * 32 + 16 * HALF + 4 * ((lane & 15) >> 2);
+    __bf16* hbase = static_cast<__bf16*>(p.out) + nb * 32 + 4 * ((lane & 15) >> 2);
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      float hv[4];
       bool real[4];
+      int re[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + i;
         const int id = p.sorted[prow];
         real[i] = (unsigned)id < (unsigned)p.n_slots;
-        const int re = real[i] ? p.row_exp[id / p.topk] : 0;  // padding rows: never stored
-        hv[i] = silu_mul(__builtin_amdgcn_ldexpf(acc[rb][0][i], re + ce0),
-                         __builtin_amdgcn_ldexpf(acc[rb][1][i], re + ce1));
+        re[i] = real[i] ? p.row_exp[id / p.topk] : 0;  // padding rows: never stored
       }
-      quad_transpose(hv, lane);
       const bool mine = q == 0 ? real[0] : q == 1 ? real[1] : q == 2 ? real[2] : real[3];
-      if (mine) {
-        const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + q;
-        *reinterpret_cast<bf16x4*>(hbase + (int64_t)prow * p.out_ld) =
-            bf16x4{(__bf16)hv[0], (__bf16)hv[1], (__bf16)hv[2], (__bf16)hv[3]};
+      const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + q;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hv[i] = silu_mul(__builtin_amdgcn_ldexpf(acc[rb][cb][i], re[i] + ce[cb]),
+                           __builtin_amdgcn_ldexpf(acc[rb][cb + 2][i], re[i] + ce[cb + 2]));
+        quad_transpose(hv, lane);
+        if (mine)
+          *reinterpret_cast<bf16x4*>(hbase + (int64_t)prow * p.out_ld + 16 * cb) =
+              bf16x4{(__bf16)hv[0], (__bf16)hv[1], (__bf16)hv[2], (__bf16)hv[3]};
       }
     }
     return;
   }
+  // down with bf16 output rows (the expert-grouped layouts)
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) {
 #pragma unroll
@@ -363,21 +420,10 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
       const int prow = mb * kTileM + 16 * rb + 4 * (lane >> 4) + i;
       const int id = p.sorted[prow];
       if ((unsigned)id >= (unsigned)p.n_slots) continue;
-      const int re = p.row_exp[MODE == kGateUp ? id / p.topk : prow];
-      const float v0 = __builtin_amdgcn_ldexpf(acc[rb][0][i], re + ce0);
-      const float v1 = __builtin_amdgcn_ldexpf(acc[rb][1][i], re + ce1);
-      if (MODE == kGateUp) {
-        __bf16* h = static_cast<__bf16*>(p.out) + (int64_t)prow * p.out_ld + nb * 32 + 16 * HALF + (lane & 15);
-        h[0] = (__bf16)silu_mul(v0, v1);
-      } else if (p.out_bf16) {
-        __bf16* o = static_cast<__bf16*>(p.out) + (int64_t)id * p.out_ld + pc0;
-        o[0] = (__bf16)v0;
-        o[32] = (__bf16)v1;
-      } else {
-        float* y = static_cast<float*>(p.out) + (int64_t)id * p.out_ld + pc0;
-        y[0] = v0;
-        y[32] = v1;
-      }
+      const int re = p.row_exp[prow];
+      __bf16* o = static_cast<__bf16*>(p.out) + (int64_t)id * p.out_ld + pc0;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) o[16 * cb] = (__bf16)__builtin_amdgcn_ldexpf(acc[rb][cb][i], re + ce[cb]);
     }
   }
 }
@@ -404,13 +450,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
     const int e = p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
 
-    // this wave copies A row block `wave` (rows 16 wave .. 16 wave + 15);
-    // padding rows read the block's first row (their results are discarded)
+    // this wave copies A row blocks kABlocksPerWave * wave + t; padding rows
+    // read the block's first row (their results are discarded)
     TileCtx c;
-    c.copy_nb = wave >> 1;
-    c.copy_j = wave & 1;
-    {
-      const int prow = mb * kTileM + 16 * wave + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < kABlocksPerWave; ++t) {
+      const int prow = mb * kTileM + 16 * (kABlocksPerWave * wave + t) + (lane & 15);
       const int id = p.sorted[prow];
       const bool real = (unsigned)id < (unsigned)p.n_slots;
       int64_t src;
@@ -420,14 +465,13 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
       } else {
         src = real ? prow : mb * kTileM;
       }
-      c.a_src = reinterpret_cast<const uint8_t*>(p.a16 + src * p.K) + 16 * (lane >> 4);
+      c.a_src[t] = reinterpret_cast<const uint8_t*>(p.a16 + src * p.K) + 16 * (lane >> 4);
     }
-    const int64_t unit_copy = ((int64_t)e * NB + nt * kTileNBlocks + c.copy_nb) * G;
-    c.wq = p.wq + unit_copy * kNibUnitBytes;
-    c.ws = reinterpret_cast<const uint8_t*>(p.ws16 + unit_copy * kScaleUnitElems);
+    const int64_t unit = ((int64_t)e * NB + nt * kTileNBlocks + wave) * G;
+    c.wq = p.wq + unit * kNibUnitBytes + 16 * lane;
+    c.ws = reinterpret_cast<const uint8_t*>(p.ws16 + unit * kScaleUnitElems) + 4 * lane;
 
-    if (wave & 1) tile_body<MODE, 1>(p, c, ring, nstages, mb, nt, e, wave, lane);
-    else tile_body<MODE, 0>(p, c, ring, nstages, mb, nt, e, wave, lane);
+    tile_body<MODE>(p, c, ring, nstages, mb, nt, e, wave, lane);
   }
 }
 
