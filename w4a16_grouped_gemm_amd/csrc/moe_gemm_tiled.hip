@@ -30,14 +30,15 @@
 // such tiny elements in h routinely; they cannot move a result that the fp32
 // sum resolves.
 //
-// Tile: a 256-thread workgroup (4 waves) computes 128 rows x 256 channels (four
-// 64-channel n-blocks) over the whole reduction. Wave w owns all 128 rows and
-// the four 16-channel column blocks of n-block w (for gate_up: gate channels in
-// blocks 0, 1 and the matching up channels in 2, 3), so each weight is
-// dequantised by exactly one wave and feeds 8 row blocks of MFMAs, and each A
-// fragment read from LDS feeds 4 MFMAs. The K loop moves in stages of two groups:
+// Tile: a 512-thread workgroup (8 waves) computes 128 rows x 512 channels
+// (eight 64-channel n-blocks) over the whole reduction; a half tile (256
+// channels) uses four of the waves. Wave w owns all 128 rows and the four
+// 16-channel column blocks of n-block w (for gate_up: gate channels in blocks
+// 0, 1 and the matching up channels in 2, 3), so each weight is dequantised by
+// exactly one wave and feeds 8 row blocks of MFMAs, and each A fragment read
+// from LDS feeds 4 MFMAs. The K loop moves in stages of two groups:
 //   A  128 rows x 64 k of fp16 (16 KiB), gathered through sorted_token_ids and
-//      shared by the four waves,
+//      shared by the waves of the tile,
 //   B  per wave, its own n-block's 2 groups of packed nibbles (2 KiB) and fp16
 //      scales (256 B),
 // copied global -> LDS by global_load_lds_dwordx4 / _dword (no VGPRs in flight)
@@ -49,9 +50,6 @@
 // fragments need every wave's copies, published by one workgroup barrier per
 // stage, which also proves the slot refilled next has been consumed.
 //
-// Tile order is XCD-aware: workgroup b runs on XCD b % 8, and the tiles an
-// XCD runs are the n-tiles of the row blocks mb = xcd (mod 8), so a row block's
-// A tile is shared through that XCD's L2.
 #include "internal.h"
 
 #include <algorithm>
@@ -66,23 +64,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStages = 3;           // LDS ring depth
+constexpr int kStages = 3;            // LDS ring depth
 constexpr int kTileM = 128;
 constexpr int kRowBlocks = kTileM / 16;
-constexpr int kTileNBlocks = kWaves;  // 4 x 64 = 256 channels, one n-block per wave
+constexpr int kTileNBlocks = kWaves;  // full tile: 8 x 64 = 512 channels, one n-block per wave
+constexpr int kHalfNBlocks = kTileNBlocks / 2;
 constexpr int kStageGroups = 2;       // 64 k per stage
 constexpr int kABytes = kTileM * kStageGroups * kGroup * 2;                  // 16 KiB
 constexpr int kBWaveBytes = kStageGroups * kNibUnitBytes;                    // 2 KiB
 constexpr int kSWaveBytes = kStageGroups * kScaleUnitElems * 2;              // 256 B
 constexpr int kBOffset = kABytes;
 constexpr int kSOffset = kABytes + kWaves * kBWaveBytes;
-constexpr int kStageBytes = kSOffset + kWaves * kSWaveBytes;                 // 25 KiB
-constexpr int kABlocksPerWave = kRowBlocks / kWaves;                         // row blocks a wave copies
+constexpr int kStageBytes = kSOffset + kWaves * kSWaveBytes;                 // 34 KiB
+// row blocks a wave copies when nw waves work on the tile
+constexpr int a_blocks_per_wave(int nw) { return kRowBlocks / nw; }
 // copies per wave and stage: its A row blocks x groups, its nibbles (one per
 // group) and its scales (both groups in one)
-constexpr int kCopiesPerWaveStage = kABlocksPerWave * kStageGroups + kStageGroups + 1;
+constexpr int copies_per_wave_stage(int nw) { return a_blocks_per_wave(nw) * kStageGroups + kStageGroups + 1; }
 // A fragments read ahead of the MFMAs that use them
 constexpr int kAhead = 4;
 // Weights and scales are read once per tile: copied with the non-temporal
@@ -193,15 +193,25 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until this wave's copies of a stage landed while the copies of
+// `later` stages issued after it may still be in flight (0 <= later < kStages - 1).
+template <int NW>
+__device__ __forceinline__ void wait_stage(int later) {
+  static_assert(kStages <= 4, "wait_stage covers up to two later stages");
+  if (kStages > 3 && later >= 2) wait_vmcnt<2 * copies_per_wave_stage(NW)>();
+  else if (later >= 1) wait_vmcnt<copies_per_wave_stage(NW)>();
+  else wait_vmcnt<0>();
+}
+
 struct TileCtx {
-  const uint8_t* a_src[kABlocksPerWave];  // this lane's A copy sources (row start + 16-byte k offset)
-  const uint8_t* wq;                      // this wave's n-block: nibble units from group 0, + 16 lane
-  const uint8_t* ws;                      // this wave's n-block: fp16 scale units from group 0, + 4 lane
+  const uint8_t* a_src[a_blocks_per_wave(kWaves / 2)];  // this lane's A copy sources (row start + 16-byte k offset)
+  const uint8_t* wq;  // this wave's n-block: nibble units from group 0, + 16 lane
+  const uint8_t* ws;  // this wave's n-block: fp16 scale units from group 0, + 4 lane
 };
 
 // Issue this wave's copies of stage `s` (groups 2s, 2s+1) into ring slot `slot`:
-// its own nibbles and scales, then its share of the A row blocks.
-__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int slot, int s, int wave) {
+// its own nibbles and scales, then its share (nab row blocks) of the A tile.
+__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int slot, int s, int wave, int nab) {
   uint8_t* base = ring + slot * kStageBytes;
   const int g0 = s * kStageGroups;
 #pragma unroll
@@ -213,19 +223,20 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int
   __builtin_amdgcn_global_load_lds(c.ws + (int64_t)g0 * (kScaleUnitElems * 2),
                                    LDS_PTR(base + kSOffset + wave * kSWaveBytes), 4, 0, kNonTemporal);
 #pragma unroll
-  for (int t = 0; t < kABlocksPerWave; ++t)
+  for (int t = 0; t < nab; ++t)
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) {
-      const int rb = kABlocksPerWave * wave + t;
+      const int rb = nab * wave + t;
       __builtin_amdgcn_global_load_lds(c.a_src[t] + (int64_t)(g0 + j) * (kGroup * 2),
                                        LDS_PTR(base + (rb * kStageGroups + j) * 1024), 16, 0, 0);
     }
 }
 
-// The K loop and epilogue of one tile for the wave owning n-block nt * 4 + wave.
-template <int MODE>
-__device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c, uint8_t* ring, int nstages, int mb,
-                                          int nt, int e, int wave, int lane) {
+// The K loop and epilogue of one tile (NW waves, NW n-blocks from nb0) for the
+// wave owning n-block nb0 + wave.
+template <int MODE, int NW>
+__device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c, uint8_t* ring, int nstages,
+                                          int mb, int nb0, int e, int wave, int lane) {
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   uint32_t magic = kF16_1024;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
@@ -256,12 +267,11 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
   ring_barrier();
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < nstages) issue_stage(c, ring, s, s, wave);
+    if (s < nstages) issue_stage(c, ring, s, s, wave, a_blocks_per_wave(NW));
 
   // stage 0's first group, dequantised before the loop, and its second
   // group's nibbles and scales (own copies only)
-  if (1 < nstages) wait_vmcnt<kCopiesPerWaveStage>();
-  else wait_vmcnt<0>();
+  wait_stage<NW>(min(nstages, kStages - 1) - 1);
   f16x8 w[4];
   u32x4 nib1 = nib_of(0, 1);
   u32x2 sc1 = sc_of(0, 1);
@@ -277,7 +287,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     // every wave waited for its own copies of stage s before this barrier;
     // everyone also finished reading stage s - 1, whose slot is refilled here
     ring_barrier();
-    if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave);
+    if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave, a_blocks_per_wave(NW));
 
     // Software pipeline inside the stage: while a group's MFMAs run, the wave
     // reads the A fragments kAhead row blocks ahead and dequantises the next
@@ -316,8 +326,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     __builtin_amdgcn_sched_barrier(0);
     // own copies of stage s + 1 landed (stage s + 2 may still be in flight);
     // after the last stage the reads below see a stale slot whose values are unused
-    if (s + 2 < nstages) wait_vmcnt<kCopiesPerWaveStage>();
-    else wait_vmcnt<0>();
+    wait_stage<NW>(min(nstages, s + kStages) - (s + 2));
     {
       // the next stage's weights: the first group is dequantised under this
       // group's MFMAs, the second is read now for the next stage's first group
@@ -343,7 +352,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
 
   // Epilogue: rows 16 rb + 4 (lane >> 4) + i of the tile; packed channels
   // 64 nb + 16 cb + (lane & 15).
-  const int nb = nt * kTileNBlocks + wave;
+  const int nb = nb0 + wave;
   const int pc0 = nb * kNBlock + (lane & 15);
   const int32_t* cexp = p.col_exp + (int64_t)e * p.N;
   int ce[4];
@@ -428,6 +437,46 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
   }
 }
 
+// Sets up a wave's copy sources for the tile (row block mb, NW n-blocks from
+// nb0) and runs it: the wave copies A row blocks a_blocks_per_wave(NW) * wave + t;
+// padding rows read the block's first row (their results are discarded).
+template <int MODE, int NW>
+__device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* ring, int nstages, int mb, int nb0, int e,
+                                         int wave, int lane) {
+  const int G = p.K / kGroup;
+  TileCtx c;
+#pragma unroll
+  for (int t = 0; t < a_blocks_per_wave(NW); ++t) {
+    const int prow = mb * kTileM + 16 * (a_blocks_per_wave(NW) * wave + t) + (lane & 15);
+    const int id = p.sorted[prow];
+    const bool real = (unsigned)id < (unsigned)p.n_slots;
+    int64_t src;
+    if (MODE == kGateUp) {
+      const int id0 = p.sorted[mb * kTileM];
+      src = (real ? id : id0) / p.topk;
+    } else {
+      src = real ? prow : mb * kTileM;
+    }
+    c.a_src[t] = reinterpret_cast<const uint8_t*>(p.a16 + src * p.K) + 16 * (lane >> 4);
+  }
+  const int64_t unit = ((int64_t)e * (p.N / kNBlock) + nb0 + wave) * G;
+  c.wq = p.wq + unit * kNibUnitBytes + 16 * lane;
+  c.ws = reinterpret_cast<const uint8_t*>(p.ws16 + unit * kScaleUnitElems) + 4 * lane;
+  tile_body<MODE, NW>(p, c, ring, nstages, mb, nb0, e, wave, lane);
+}
+
+// Persistent workgroups of 8 waves. Work items are full tiles (128 rows x 512
+// channels, 8 waves) and half tiles (128 x 256, 4 waves; the other 4 take the
+// same barriers and nothing else). A row block's channels are its full tiles
+// plus, when N / 64 is an odd multiple of 4, one half tile at the end.
+//
+// Tile order is XCD-aware: workgroup b runs on XCD b % 8, and the items an XCD
+// runs are those of the row blocks mb = xcd (mod 8), so a row block's A tile
+// is shared through that XCD's L2. An XCD's full tiles run in rounds of one
+// per workgroup; when the last round would leave at least half of the XCD's
+// workgroups idle, its tiles run as twice as many half tiles instead, one per
+// workgroup (a workgroup with half a tile runs it faster than a full one, and
+// every CU keeps a share of the round).
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
@@ -436,42 +485,47 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_tiled_kernel(GemmParams p) 
   const int ntpp = min(*p.ntpp, p.capacity);
   const int n_mblocks = ntpp / kTileM;
   const int NB = p.N / kNBlock;
-  const int NT = NB / kTileNBlocks;  // n-tiles per row block
-  const int G = p.K / kGroup;
-  const int nstages = G / kStageGroups;
+  const int F = NB / kTileNBlocks;                      // full tiles per row block
+  const int Ht = (NB % kTileNBlocks) ? 1 : 0;           // trailing half tile per row block
+  const int nstages = p.K / kGroup / kStageGroups;
 
-  // XCD-aware order: local tile index q of XCD x covers row block x + 8 (q / NT).
   const int xcd = (int)blockIdx.x & 7;
   const int per_xcd = (int)gridDim.x >> 3;  // grid is a multiple of 8
-  const int q_total = ((n_mblocks + 7 - xcd) / 8) * NT;
-  for (int q = (int)blockIdx.x >> 3; q < q_total; q += per_xcd) {
-    const int mb = xcd + 8 * (q / NT);
-    const int nt = q - (q / NT) * NT;
+  const int nmb = (n_mblocks + 7 - xcd) / 8;  // row blocks of this XCD: xcd + 8 j
+  const int nfull = nmb * F;
+  const int rounds = nfull / per_xcd, rem = nfull - rounds * per_xcd;
+  const bool split = rem > 0 && 2 * rem <= per_xcd;
+  const int n_full_items = split ? rounds * per_xcd : nfull;
+  const int n_split_halves = split ? 2 * rem : 0;
+  const int n_items = n_full_items + n_split_halves + nmb * Ht;
+  for (int i = (int)blockIdx.x >> 3; i < n_items; i += per_xcd) {
+    int j, nb0;
+    bool half;
+    if (i < n_full_items) {
+      j = i / F;
+      nb0 = (i - j * F) * kTileNBlocks;
+      half = false;
+    } else if (i < n_full_items + n_split_halves) {
+      const int h = i - n_full_items, q = n_full_items + h / 2;
+      j = q / F;
+      nb0 = (q - j * F) * kTileNBlocks + (h & 1) * kHalfNBlocks;
+      half = true;
+    } else {
+      j = i - n_full_items - n_split_halves;
+      nb0 = F * kTileNBlocks;
+      half = true;
+    }
+    const int mb = xcd + 8 * j;
     const int e = p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
-
-    // this wave copies A row blocks kABlocksPerWave * wave + t; padding rows
-    // read the block's first row (their results are discarded)
-    TileCtx c;
-#pragma unroll
-    for (int t = 0; t < kABlocksPerWave; ++t) {
-      const int prow = mb * kTileM + 16 * (kABlocksPerWave * wave + t) + (lane & 15);
-      const int id = p.sorted[prow];
-      const bool real = (unsigned)id < (unsigned)p.n_slots;
-      int64_t src;
-      if (MODE == kGateUp) {
-        const int id0 = p.sorted[mb * kTileM];
-        src = (real ? id : id0) / p.topk;
-      } else {
-        src = real ? prow : mb * kTileM;
-      }
-      c.a_src[t] = reinterpret_cast<const uint8_t*>(p.a16 + src * p.K) + 16 * (lane >> 4);
+    if (!half) {
+      run_tile<MODE, kWaves>(p, ring, nstages, mb, nb0, e, wave, lane);
+    } else if (wave < kWaves / 2) {
+      run_tile<MODE, kWaves / 2>(p, ring, nstages, mb, nb0, e, wave, lane);
+    } else {
+      // the barriers of the half tile: one before its prologue, one per stage
+      for (int s = 0; s <= nstages; ++s) ring_barrier();
     }
-    const int64_t unit = ((int64_t)e * NB + nt * kTileNBlocks + wave) * G;
-    c.wq = p.wq + unit * kNibUnitBytes + 16 * lane;
-    c.ws = reinterpret_cast<const uint8_t*>(p.ws16 + unit * kScaleUnitElems) + 4 * lane;
-
-    tile_body<MODE>(p, c, ring, nstages, mb, nt, e, wave, lane);
   }
 }
 
@@ -558,7 +612,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void rows_to_f16_kernel(
 template <int MODE>
 hipError_t launch_tiled_mode(const GemmParams& p, hipStream_t stream) {
   const int64_t mblocks_max = p.capacity / kTileM;
-  const int64_t tiles_max = mblocks_max * (p.N / (kNBlock * kTileNBlocks));
+  const int NB = p.N / kNBlock;
+  const int64_t tiles_max = mblocks_max * (NB / kTileNBlocks + (NB % kTileNBlocks ? 1 : 0));
   if (tiles_max == 0) return hipSuccess;
   static int blocks_per_cu = [] {
     // the LDS ring exceeds the default 64 KiB dynamic limit
@@ -583,7 +638,7 @@ hipError_t launch_tiled_mode(const GemmParams& p, hipStream_t stream) {
 }  // namespace
 
 bool tiled_gemm_supported(int32_t block_m, int32_t N, int32_t K) {
-  return block_m == kTileM && (K / kGroup) % kStageGroups == 0 && N % (kNBlock * kTileNBlocks) == 0;
+  return block_m == kTileM && (K / kGroup) % kStageGroups == 0 && N % (kNBlock * kHalfNBlocks) == 0;
 }
 
 size_t tiled_scratch_bytes(int64_t rows, int32_t K) {
