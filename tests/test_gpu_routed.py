@@ -150,6 +150,28 @@ def test_routed_graph_replays():
         del junk
 
 
+@pytest.mark.parametrize("T,topk,E,Eg,I,seed", [
+    (128, 8, 48, 384, 256, 41),   # the decode shape: 1024 routed ids, the largest call aligned in gate_up
+    (1, 8, 48, 384, 256, 42),     # one token
+    (16, 4, 64, 64, 256, 43),     # every routed expert local, 64 of them
+    (40, 6, 5, 40, 128, 44),      # few local experts, most ids elsewhere
+])
+def test_routed_alignment_inside_gate_up(T, topk, E, Eg, I, seed):
+    """Decode-sized calls at block_m 16 align their ids inside the gate_up launch (every
+    workgroup sorts them in LDS, workgroup 0 also writes the buffers the down GEMM reads): the
+    layer must equal, bit for bit, moe_align + w4a16_moe_forward at block_m 16, and the oracle."""
+    c = synthetic.random_case("fused_align", T=T, H=2048, I=I, E=E, topk=topk, block_m=16, seed=seed, E_global=Eg)
+    d = DeviceCase(c)
+    assert w.w4a16_choose_block_m(c.T, c.topk, c.E, Eg) == 16
+    assert w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg) == 0
+    say(f"routed with in-launch alignment T={T} topk={topk} E={E}/{Eg}")
+    out = routed(d, Eg)
+    assert np.array_equal(out, d.forward(16)), "differs from a separate alignment"
+    ref = oracle.moe_layer(c.x, c.topk_ids, c.topk_weights, c.w13_q, c.w13_s, c.w2_q, c.w2_s, c.E, c.I)
+    parity(out, ref, f"routed in-launch alignment T={T}")
+    assert np.array_equal(out, routed(d, Eg)), "run-to-run difference"
+
+
 def test_routed_single_alignment_equals_forward():
     c = synthetic.workload("tiny")
     d = DeviceCase(c)

@@ -636,28 +636,42 @@ int w4a16_moe_routed_forward(const w4a16_moe_shape* shape, const uint16_t* x, in
   float* y = reinterpret_cast<float*>(ws + r.y);
   void* scratch = ws + r.scratch;
   void* hist = ws + r.hist;
-  if (r.split)  // both sets in one pass over the ids
-    st = hip_status(launch_align_split(topk_ids, T * topk, E, kHeavyRows, sorted[0], r.set[0].block_m,
-                                       r.set[0].capacity, eids[0], ntpp[0], r.set[1].block_m, r.set[1].capacity,
-                                       eids[1], ntpp[1], hist, hs));
-  else
-    st = hip_status(launch_align(topk_ids, T * topk, E, r.set[0].block_m, sorted[0], r.set[0].capacity, eids[0],
-                                 ntpp[0], nullptr, hist, hs));
-  if (st != W4A16_OK) return st;
-  st = w4a16_moe_prepare_x(shape, x, T, topk, topk_ids, r.set[0].block_m, scratch, r.scratch_bytes, stream);
-  if (st != W4A16_OK) return st;
   const int32_t H = shape->hidden, I = shape->intermediate;
   // the light set's capacity is below moe_align_capacity, so its GEMMs are launched here directly
-  const auto gemm = [&](GemmMode mode, int k) {
+  const auto gemm_params_of = [&](GemmMode mode, int k) {
     const bool up = mode == kGateUp;
     GemmParams p = gemm_params(shape, T, topk, sorted[k], r.set[k].gemm_rows, eids[k], ntpp[k],
                                up ? w13_packed : w2_packed, up ? 2 * I : H, up ? H : I);
     p.a = up ? x : h[k];
     p.out = up ? static_cast<void*>(h[k]) : static_cast<void*>(y);
     p.out_ld = up ? I : H;
-    return hip_status(launch_moe_gemm(mode, r.set[k].block_m, p, scratch, hs));
+    return p;
   };
-  for (int k = 0; k < nsets; ++k)
+  const auto gemm = [&](GemmMode mode, int k) {
+    return hip_status(launch_moe_gemm(mode, r.set[k].block_m, gemm_params_of(mode, k), scratch, hs));
+  };
+  // Decode-sized calls at block_m 16: the alignment runs inside the gate_up
+  // launch (one launch less on the path); otherwise it is a launch of its own.
+  bool aligned_in_gate_up = false;
+  if (!r.split && r.set[0].block_m == 16) {
+    const hipError_t e = launch_gate_up_fused_align(gemm_params_of(kGateUp, 0), topk_ids, T * topk, sorted[0],
+                                                    eids[0], ntpp[0], hs);
+    if (e == hipSuccess) aligned_in_gate_up = true;
+    else if (e != hipErrorNotSupported) return hip_status(e);
+  }
+  if (!aligned_in_gate_up) {
+    if (r.split)  // both sets in one pass over the ids
+      st = hip_status(launch_align_split(topk_ids, T * topk, E, kHeavyRows, sorted[0], r.set[0].block_m,
+                                         r.set[0].capacity, eids[0], ntpp[0], r.set[1].block_m, r.set[1].capacity,
+                                         eids[1], ntpp[1], hist, hs));
+    else
+      st = hip_status(launch_align(topk_ids, T * topk, E, r.set[0].block_m, sorted[0], r.set[0].capacity, eids[0],
+                                   ntpp[0], nullptr, hist, hs));
+    if (st != W4A16_OK) return st;
+  }
+  st = w4a16_moe_prepare_x(shape, x, T, topk, topk_ids, r.set[0].block_m, scratch, r.scratch_bytes, stream);
+  if (st != W4A16_OK) return st;
+  for (int k = aligned_in_gate_up ? 1 : 0; k < nsets; ++k)
     if ((st = gemm(kGateUp, k)) != W4A16_OK) return st;
   st = w4a16_moe_prepare_h(shape, T, topk, h[0], sorted[0], r.set[0].gemm_rows, ntpp[0], r.set[0].block_m, scratch,
                            r.scratch_bytes, stream);

@@ -147,6 +147,14 @@ hipError_t launch_moe_gemm_tiled(GemmMode mode, const GemmParams& p, void* scrat
 bool stream_lds_supported(int32_t block_m, const GemmParams& p);
 hipError_t launch_moe_gemm_stream_lds(GemmMode mode, int32_t block_m, const GemmParams& p, hipStream_t stream);
 
+// The block_m 16 gate_up GEMM with the alignment of its n routed ids done
+// inside the same launch (n <= 1024 over E <= 64 experts; p.sorted,
+// p.expert_ids, p.ntpp are ignored): sorted, expert_ids and ntpp (capacity
+// p.capacity) are written as launch_align writes them, for the down GEMM.
+// hipErrorNotSupported, with nothing launched, when the shape is outside that.
+hipError_t launch_gate_up_fused_align(const GemmParams& p, const int32_t* ids, int32_t n, int32_t* sorted,
+                                      int32_t* expert_ids, int32_t* ntpp, hipStream_t stream);
+
 hipError_t launch_combine(const int32_t* ids, const float* w, const float* y, uint16_t* out, int32_t T,
                           int32_t topk, int32_t H, int32_t E, hipStream_t stream);
 

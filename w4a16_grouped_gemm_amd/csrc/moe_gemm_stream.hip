@@ -169,14 +169,137 @@ __device__ __forceinline__ void issue_batch(u32x4 (&nib)[U], int slot, int a_slo
     nib[uu] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wq + (int64_t)(g0 + uu) * kNibUnitBytes));
 }
 
+// ---- alignment inside the gate_up launch (decode-sized calls) ---------------
+// For a few routed ids (n <= kFuseMaxIds over E <= kFuseMaxExperts local
+// experts, block_m 16) the alignment is cheaper to redo in every workgroup of
+// the gate_up launch than to run as a launch of its own ahead of it: each
+// workgroup sorts the ids in LDS exactly as moe_align does (stable counting
+// sort, blocks of 16 rows padded with the sentinel n, experts in order),
+// keeps its own units' row ids and experts, and workgroup 0 also writes
+// sorted_token_ids, expert_ids and num_tokens_post_padded for the down GEMM.
+constexpr int kFuseMaxIds = 1024;
+constexpr int kFuseMaxExperts = 64;
+constexpr int kFuseMaxUnitsPerWg = 4;
+constexpr int kFuseVWaves = kFuseMaxIds / 64;  // 64-id slices of the ids, in order
+constexpr int kUnitTab = 17;                   // per unit: expert, then its 16 row ids
+
+struct FusedAlign {
+  const int32_t* ids;  // topk_ids, n of them
+  int n;
+  int32_t* sorted;  // outputs as moe_align writes them (capacity p.capacity)
+  int32_t* expert_ids;
+  int32_t* ntpp;
+};
+
+// Bytes of LDS the in-launch alignment uses before the weight stream starts
+// (inside the A ring): per-slice counts, offsets, the sorted rows and the
+// block experts.
+__host__ __device__ constexpr size_t fused_align_scratch_bytes(int capacity) {
+  return 4 * ((size_t)kFuseVWaves * kFuseMaxExperts + kFuseMaxExperts + 1 + (size_t)capacity + (capacity + 15) / 16);
+}
+
+// Returns num_tokens_post_padded; fills tab[k] (k < units of this workgroup)
+// with the expert and the 16 row ids of unit u_begin + k. All 256 threads.
+__device__ int fused_align(const FusedAlign& fa, int E, int capacity, int NG, int* scratch, int* tab) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = (capacity + 15) / 16;
+  int* wcnt = scratch;                              // [slice][expert]
+  int* off = wcnt + kFuseVWaves * kFuseMaxExperts;  // [expert], then the padded total
+  int* srt = off + kFuseMaxExperts + 1;             // [capacity]
+  int* ex = srt + capacity;                         // [nblk]
+  for (int i = tid; i < kFuseVWaves * kFuseMaxExperts; i += kThreads) wcnt[i] = 0;
+  for (int i = tid; i < capacity; i += kThreads) srt[i] = fa.n;
+  for (int i = tid; i < nblk; i += kThreads) ex[i] = -1;
+  constexpr int kRounds = kFuseMaxIds / kThreads;
+  int v[kRounds], rank[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int j = r * kThreads + tid;
+    v[r] = j < fa.n ? fa.ids[j] : -1;
+  }
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  // slice r * 4 + wave holds ids [64 (r * 4 + wave), +64): ranks by ballot over the expert bits
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int e = v[r];
+    const bool local = (unsigned)e < (unsigned)E;
+    uint64_t peers = __ballot(local);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(local && bit);
+      peers &= bit ? m : ~m;
+    }
+    rank[r] = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0));
+    if (local && rank[r] == 0) wcnt[(r * 4 + wave) * kFuseMaxExperts + e] = __popcll(peers);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  if (wave == 0) {
+    // lane e: the expert's count before each slice, its padded size, its offset
+    int before = 0;
+    for (int q = 0; q < kFuseVWaves; ++q) {
+      const int c = wcnt[q * kFuseMaxExperts + lane];
+      wcnt[q * kFuseMaxExperts + lane] = before;
+      before += c;
+    }
+    const int pc = lane < E ? (before + 15) & ~15 : 0;
+    int incl = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const int o = incl - pc;
+    off[lane] = o;
+    if (lane == 63) off[kFuseMaxExperts] = incl;
+    for (int b = o / 16; b < (o + pc) / 16 && b < nblk; ++b) ex[b] = lane;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int e = v[r];
+    if ((unsigned)e < (unsigned)E) {
+      const int pos = off[e] + wcnt[(r * 4 + wave) * kFuseMaxExperts + e] + rank[r];
+      if (pos < capacity) srt[pos] = r * kThreads + tid;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  const int ntpp = min(off[kFuseMaxExperts], capacity);
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < capacity; i += kThreads) fa.sorted[i] = srt[i];
+    for (int i = tid; i < nblk; i += kThreads) fa.expert_ids[i] = ex[i];
+    if (tid == 0) *fa.ntpp = ntpp;
+  }
+  const int units = ntpp / 16 * NG;
+  const int per_wg = (units + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int u_begin = (int)blockIdx.x * per_wg;
+  const int nu = min(min(units - u_begin, per_wg), kFuseMaxUnitsPerWg);
+  for (int i = tid; i < nu * kUnitTab; i += kThreads) {
+    const int k = i / kUnitTab, j = i - k * kUnitTab;
+    const int mb = (u_begin + k) / NG;
+    tab[i] = j == 0 ? ex[mb] : srt[mb * 16 + j - 1];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  return ntpp;
+}
+
 // MULTI: KN > 1 (n-block boundaries inside the batch loop); otherwise KN == 1
 // and the single n-block is stored after the loop, which keeps the common
 // long-K kernel's register count where it was. With MULTI and K / 32 <= U x DEPTH
 // groups the row block's A fragments for the whole of K fit the A ring: they
 // are copied during the first n-block only and stay resident for the others.
-template <int MODE, int RB, int U, int DEPTH, bool MULTI, int KS>
-__global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p, int KN) {
+// ALIGN: the alignment runs inside this launch (fused_align; RB 1, no MULTI):
+// expert and row ids come from the workgroup's unit table in LDS.
+template <int MODE, int RB, int U, int DEPTH, bool MULTI, int KS, bool ALIGN = false>
+__global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParams p, int KN, FusedAlign fa) {
   static_assert(KS == 1 || ((KS == 2 || KS == 4) && !MULTI), "a split reduction runs one n-block per wave");
+  static_assert(!ALIGN || (RB == 1 && !MULTI), "the in-launch alignment serves 16-row units");
   using C = Cfg<RB, U, DEPTH, KS>;
   constexpr int BM = 16 * RB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -186,11 +309,13 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
   uint8_t* a_ring = lds;
   uint8_t* s_ring = lds + DEPTH * C::kABatchBytes + wave * DEPTH * C::kSBatchBytes;
   int* row_ids = reinterpret_cast<int*>(lds + DEPTH * C::kABatchBytes + 4 * DEPTH * C::kSBatchBytes);
+  int* unit_tab = row_ids + C::kIdsBytes / 4;  // ALIGN only
 
-  const int ntpp = min(*p.ntpp, p.capacity);
-  const int n_mblocks = ntpp / BM;
   const int NB = p.N / kNBlock;
   const int NG = NB / (kUnitNBlocks / KS * KN);  // units per row block
+  const int ntpp = ALIGN ? fused_align(fa, p.E, p.capacity, NG, reinterpret_cast<int*>(lds), unit_tab)
+                         : min(*p.ntpp, p.capacity);
+  const int n_mblocks = ntpp / BM;
   const int G = p.K / kGroup;
   const int Gw = G / KS;                    // groups of one n-block this wave reduces
   const int kh = KS > 1 ? wave % KS : 0;    // which part of K
@@ -209,7 +334,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
   for (int unit = u_begin; unit < u_end; ++unit) {
     const int mb = unit / NG;
     const int ng = unit - mb * NG;
-    const int e = p.expert_ids[mb];
+    const int* tab = unit_tab + (unit - u_begin) * kUnitTab;  // ALIGN only
+    const int e = ALIGN ? tab[0] : p.expert_ids[mb];
     if ((unsigned)e >= (unsigned)p.E) continue;  // uniform across the workgroup
     const int nb0 = (ng * (kUnitNBlocks / KS) + wave / KS) * KN;  // this wave's first n-block
 
@@ -224,11 +350,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
       const int khj = KS > 1 ? j / (RB * U) : 0, jj = KS > 1 ? j % (RB * U) : j;
       const int rb = jj / U, uu = jj % U;
       const int prow = mb * BM + rb * 16 + (lane & 15);
-      const int id = p.sorted[prow];
+      const int id = ALIGN ? tab[1 + rb * 16 + (lane & 15)] : p.sorted[prow];
       const bool real = (unsigned)id < (unsigned)p.n_slots;
       int64_t src;
       if (MODE == kGateUp) {
-        const int id0 = p.sorted[mb * BM];
+        const int id0 = ALIGN ? tab[1] : p.sorted[mb * BM];
         src = (real ? id : id0) / p.topk;
       } else {
         src = real ? prow : mb * BM;
@@ -256,7 +382,9 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_stream_lds_kernel(GemmParam
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible after the next barrier
     }
     const auto lds_ids = [&](int rb, int i) { return row_ids[rb * 16 + 4 * (lane >> 4) + i]; };
-    const auto mem_ids = [&](int rb, int i) { return p.sorted[mb * BM + rb * 16 + 4 * (lane >> 4) + i]; };
+    const auto mem_ids = [&](int rb, int i) {
+      return ALIGN ? tab[1 + rb * 16 + 4 * (lane >> 4) + i] : p.sorted[mb * BM + rb * 16 + 4 * (lane >> 4) + i];
+    };
 #pragma unroll
     for (int s = 0; s < DEPTH - 1; ++s)
       if (s < nbatch)
@@ -377,7 +505,7 @@ hipError_t launch_kn(const GemmParams& p, int kn, hipStream_t stream) {
   // faster for the decode down projection).
   const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu * 4);
   hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<MODE, RB, U, DEPTH, MULTI, KS>), dim3((int)grid), dim3(kThreads),
-                     C::kLdsBytes, stream, p, kn);
+                     C::kLdsBytes, stream, p, kn, FusedAlign{});
   return hipGetLastError();
 }
 
@@ -408,6 +536,40 @@ hipError_t launch_mode(int32_t block_m, const GemmParams& p, hipStream_t stream)
 }
 
 }  // namespace
+
+hipError_t launch_gate_up_fused_align(const GemmParams& p, const int32_t* ids, int32_t n, int32_t* sorted,
+                                      int32_t* expert_ids, int32_t* ntpp, hipStream_t stream) {
+  constexpr int RB = 1, U = 4, DEPTH = 3, KS = 2;
+  using C = Cfg<RB, U, DEPTH, KS>;
+  const int G = p.K / kGroup;
+  const int NB = p.N / kNBlock;
+  // the block_m 16 split configuration launch() picks for a long gate_up reduction
+  if (n < 1 || n > kFuseMaxIds || p.E > kFuseMaxExperts || !stream_lds_supported(16, p) ||
+      n_blocks_per_wave(p) != 1 || G < kSplitMinGroups || G % (2 * U) != 0 || NB % (kUnitNBlocks / KS) != 0)
+    return hipErrorNotSupported;
+  if (fused_align_scratch_bytes(p.capacity) > (size_t)DEPTH * C::kABatchBytes) return hipErrorNotSupported;
+  const int NG = NB / (kUnitNBlocks / KS);
+  const int64_t units_max = (int64_t)(p.capacity / 16) * NG;
+  if (units_max == 0) return hipErrorNotSupported;
+  constexpr int kLds = C::kLdsBytes + kFuseMaxUnitsPerWg * kUnitTab * 4;
+  static int blocks_per_cu = [] {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(moe_gemm_stream_lds_kernel<kGateUp, RB, U, DEPTH, false, KS, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, moe_gemm_stream_lds_kernel<kGateUp, RB, U, DEPTH, false, KS, true>,
+                                                     kThreads, kLds) != hipSuccess ||
+        b < 1)
+      b = 1;
+    return b;
+  }();
+  const int64_t grid = std::min<int64_t>(units_max, (int64_t)device_cu_count() * blocks_per_cu * 4);
+  if ((units_max + grid - 1) / grid > kFuseMaxUnitsPerWg) return hipErrorNotSupported;
+  const FusedAlign fa{ids, n, sorted, expert_ids, ntpp};
+  hipLaunchKernelGGL((moe_gemm_stream_lds_kernel<kGateUp, RB, U, DEPTH, false, KS, true>), dim3((int)grid),
+                     dim3(kThreads), kLds, stream, p, 1, fa);
+  return hipGetLastError();
+}
 
 bool stream_lds_supported(int32_t block_m, const GemmParams& p) {
   return (block_m == 16 || block_m == 32 || block_m == 64) && p.N % (kNBlock * kUnitNBlocks) == 0 &&
