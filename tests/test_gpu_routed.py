@@ -122,30 +122,39 @@ def test_routed_small_skewed(T, topk, E, Eg, s):
     assert np.array_equal(out, routed(d, Eg)), "run-to-run difference"
 
 
-def test_routed_graph_replays():
-    """The split call captured in a HIP graph (through torch) and replayed with eager work in
-    between: every replay equals the eager result."""
-    c = synthetic.random_case("routed_graph", T=512, H=256, I=128, E=8, topk=2, block_m=128, seed=34, E_global=16,
-                              logit_bias=synthetic.zipf_bias(16, s=1.5))
+@pytest.mark.parametrize("kind", ["split", "aligned_in_gate_up"])
+def test_routed_graph_replays(kind):
+    """The call captured in a HIP graph (through torch) and replayed with eager work in between:
+    every replay equals the eager result. split: the heavy/light prefill call; aligned_in_gate_up:
+    a decode-sized call whose alignment runs inside the gate_up launch."""
+    if kind == "split":
+        Eg = 16
+        c = synthetic.random_case("routed_graph", T=512, H=256, I=128, E=8, topk=2, block_m=128, seed=34, E_global=Eg,
+                                  logit_bias=synthetic.zipf_bias(Eg, s=1.5))
+    else:
+        Eg = 384
+        c = synthetic.random_case("routed_graph_dec", T=128, H=2048, I=256, E=48, topk=8, block_m=16, seed=35,
+                                  E_global=Eg)
     d = DeviceCase(c)
-    eager = routed(d, 16)
-    ws = torch.empty(w.w4a16_moe_routed_workspace_bytes(d.shape, c.T, c.topk, 16), dtype=torch.uint8, device="cuda")
+    assert (w.w4a16_moe_routed_split(d.shape, c.T, c.topk, Eg) > 0) == (kind == "split")
+    eager = routed(d, Eg)
+    ws = torch.empty(w.w4a16_moe_routed_workspace_bytes(d.shape, c.T, c.topk, Eg), dtype=torch.uint8, device="cuda")
     out = torch.zeros((c.T, c.H), dtype=torch.int16, device="cuda")
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        w.w4a16_moe_routed_forward(d.shape, d.x, d.ids, d.wts, 16, d.w13p, d.w2p, out, ws)  # warm-up on s
+        w.w4a16_moe_routed_forward(d.shape, d.x, d.ids, d.wts, Eg, d.w13p, d.w2p, out, ws)  # warm-up on s
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        w.w4a16_moe_routed_forward(d.shape, d.x, d.ids, d.wts, 16, d.w13p, d.w2p, out, ws)
+        w.w4a16_moe_routed_forward(d.shape, d.x, d.ids, d.wts, Eg, d.w13p, d.w2p, out, ws)
     for i in range(4):
         out.fill_(-1)
         junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
         g.replay()
         torch.cuda.synchronize()
-        say(f"routed graph replay {i}")
+        say(f"routed graph replay {kind} {i}")
         assert np.array_equal(out.cpu().numpy().view(np.uint16), eager), f"replay {i} differs"
         del junk
 
