@@ -262,6 +262,48 @@ def test_full_size_sampled(name):
     assert np.array_equal(out, d2), "run-to-run difference"
 
 
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_row(name):
+    """Every row of the full-size workload, not a sample: both GEMMs on every real aligned row
+    against the exact fp64 projections of that row's own inputs (check_own_rows), then the combine
+    of every token from the GPU's own fp32 y rows against their fp64 weighted sum (one bf16
+    rounding apart at most), and the staged sequence equal to the one-call forward bit for bit."""
+    c = synthetic.workload(name)
+    d = DeviceCase(c)
+    bm = c.block_m
+    buf = d.align(bm)
+    srt, eid, ntpp = buf["sorted_token_ids"], buf["expert_ids"], buf["num_tokens_post_padded"]
+    say(f"layer full-size every row {name}: T={c.T} slots={c.local_slots()} bm={bm} "
+        f"row blocks {int(ntpp.item()) // bm}")
+    h, y = run_stages(d, bm, srt, eid, ntpp, c.T, c.topk)
+    check_own_rows(c, c.x, h, y, srt, eid, ntpp, bm, c.topk, f"{name} full size")
+    out = torch.full((c.T, c.H), -1, dtype=torch.int16, device="cuda")
+    w.w4a16_moe_combine(d.shape, d.ids, d.wts, y, out)
+    torch.cuda.synchronize()
+    out_bits = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(out_bits, d.forward(bm)), "staged sequence differs from forward"
+    # combine: the weighted sum over resident slots of the GPU's own y rows, exact in fp64;
+    # the GPU sums in fp32 in j order (each of the <= topk additions rounds by at most 2^-24 of
+    # the sum of |w y| so far) and rounds the result to bf16 once (half an ulp, one ulp allowed)
+    yh = y.cpu().numpy().reshape(c.T, c.topk, c.H)
+    res = (c.topk_ids >= 0) & (c.topk_ids < c.E)
+    o64 = np.zeros((c.T, c.H))
+    mag = np.zeros((c.T, c.H))
+    for j in range(c.topk):
+        m = res[:, j]
+        term = c.topk_weights[m, j].astype(np.float32).astype(np.float64)[:, None] * yh[m, j].astype(np.float64)
+        o64[m] += term
+        mag[m] += np.abs(term)
+    o = bf16_to_f64(out_bits)
+    ulp = np.zeros_like(o64)
+    nz = o64 != 0
+    ulp[nz] = 2.0 ** (np.floor(np.log2(np.abs(o64[nz]))) - 7)
+    tol = ulp + c.topk * 2.0**-24 * mag
+    err = np.abs(o - o64)
+    say(f"  {name} combine of every token: max err/tol {float((err / np.maximum(tol, 1e-300)).max()):.3f}")
+    assert np.all(err <= tol), f"{name}: combine off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
+
+
 def test_split_k_several_units_per_workgroup():
     """block_m 16 at the Kimi-K2 shapes (both reductions split between two waves per
     n-block) with far more live units than the persistent grid's workgroups: 400
