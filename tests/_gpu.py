@@ -110,13 +110,14 @@ def run_stages(d, bm, srt, eid, ntpp, T, topk, row_ids=None, x=None):
     return h, y
 
 
-def check_own_rows(c, x_bits, h, y, srt, eid, ntpp, bm, topk, what):
+def check_own_rows(c, x_bits, h, y, srt, eid, ntpp, bm, topk, what, detail=False):
     """Each GEMM stage on the very rows it was given, for every real aligned row:
     h = bf16(silu(g) * u) against g, u the exact fp64 projections of the row's
     activation (within bf16 rounding plus the fp32 sum's error), and y against
     the exact fp64 projection of the GPU's own h row. Returns (rows, slots, experts,
     h rows as bf16 bits, number of h elements whose bf16 rounding differs from
-    the exact value's)."""
+    the exact value's); with detail, also per row whether any of its h elements
+    did, and the fp64 down projection of the GPU's own h rows)."""
     import oracle
 
     I, H = c.I, c.H
@@ -135,7 +136,8 @@ def check_own_rows(c, x_bits, h, y, srt, eid, ntpp, bm, topk, what):
     assert np.all(err <= tol), f"{what}: gate_up rows off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
     import synthetic
 
-    flips = int((h_bits != synthetic.to_bf16_bits(h_exact.astype(np.float32))).sum())
+    flip = h_bits != synthetic.to_bf16_bits(h_exact.astype(np.float32))
+    flips = int(flip.sum())
     y_ref = oracle.expert_rows(h_bits, ex, c.w2_q, c.w2_s, H, I)
     y_gpu = y.cpu().numpy()[slot].astype(np.float64)
     err = np.abs(y_gpu - y_ref)
@@ -143,4 +145,6 @@ def check_own_rows(c, x_bits, h, y, srt, eid, ntpp, bm, topk, what):
     say(f"  {what} down rows: max err/tol {float((err / tol).max()):.4f}; "
         f"h elements rounded to the other bf16 neighbour than the exact value: {flips}/{h_bits.size}")
     assert np.all(err <= tol), f"{what}: down rows off, e.g. {np.argwhere(err > tol)[:5].tolist()}"
+    if detail:
+        return rows, slot, ex, h_bits, flips, flip.any(axis=1), y_ref
     return rows, slot, ex, h_bits, flips
