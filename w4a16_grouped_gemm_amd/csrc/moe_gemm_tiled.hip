@@ -13,9 +13,9 @@
 //   * weights: q * s' where s' = s * 2^-E_n is the group scale normalised by a
 //     power of two per output channel (the channel's largest scale lands in
 //     [16, 32)). q has at most 3 significant bits and s' at most 8, so q * s'
-//     is an exact fp16 value; it is formed with two exact packed-fp16
-//     operations from the code (q + 8) OR-ed into the mantissa of fp16 1024.0
-//     (see dequant).
+//     is an exact fp16 value; it is formed with one exact packed-fp16 fma
+//     from the code (q + 8), rotated to bits 6-9 of a half and OR-ed into the
+//     mantissa of fp16 16.0 (see dequant_half).
 //   * activations: rows converted by rows_to_f16 with a power-of-two row factor
 //     (largest element mapped into [2^14, 2^15)).
 // Every product is exact, the sum is fp32 (as the scalar definition), and the
@@ -89,9 +89,8 @@ constexpr int kAhead = 4;
 // policy (operand 2 = nt) so they do not evict the A tile shared through L2.
 constexpr int kNonTemporal = 2;
 
-constexpr uint32_t kCodeLo = 0x000F000Fu;   // codes at bits 0-3 of each half
-constexpr uint32_t kCodeHi = 0x00F000F0u;   // codes at bits 4-7 of each half
-constexpr uint32_t kF16_1024 = 0x64006400u;  // fp16 1024.0 in both halves
+constexpr uint32_t kCodeMid = 0x03C003C0u;  // bits 6-9 of each half
+constexpr uint32_t kF16_16 = 0x4C004C00u;    // fp16 16.0 in both halves
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
   uint32_t r;
@@ -99,36 +98,28 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
   return r;
 }
 
-// Eight codes of one column block -> fp16 (code - 8) * s, exactly. A code at
-// bits 0-3 of a half OR-ed into fp16 1024.0 gives 1024 + code, one at bits 4-7
-// gives 1024 + 16 code (the mantissa's unit is 1 there), so only the upper
-// byte pairs need a shift. Subtracting 1032, resp. 1152, is exact (small
-// integers) and leaves q, resp. 16 q; times s, resp. s / 16, that is q * s
-// exactly. The four extractions, the four subtractions and the four products
-// are independent of one another within each step, so they issue back to
-// back with no dependent packed operation right behind its producer.
-__device__ __forceinline__ f16x8 dequant(uint32_t w, f16x2 s2, f16x2 s2_16, uint32_t magic) {
-  const f16x2 b_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2 b_hi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const uint32_t w8 = w >> 8;
-  f16x2 t0 = __builtin_bit_cast(f16x2, and_or(w, kCodeLo, magic));   // elements 0, 1
-  f16x2 t1 = __builtin_bit_cast(f16x2, and_or(w, kCodeHi, magic));   // elements 2, 3
-  f16x2 t2 = __builtin_bit_cast(f16x2, and_or(w8, kCodeLo, magic));  // elements 4, 5
-  f16x2 t3 = __builtin_bit_cast(f16x2, and_or(w8, kCodeHi, magic));  // elements 6, 7
-  t0 = t0 + b_lo;
-  t1 = t1 + b_hi;
-  t2 = t2 + b_lo;
-  t3 = t3 + b_hi;
-  t0 = t0 * s2;
-  t1 = t1 * s2_16;
-  t2 = t2 * s2;
-  t3 = t3 * s2_16;
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, t0);
-  r[1] = __builtin_bit_cast(uint32_t, t1);
-  r[2] = __builtin_bit_cast(uint32_t, t2);
-  r[3] = __builtin_bit_cast(uint32_t, t3);
-  return __builtin_bit_cast(f16x8, r);
+// Four of the eight codes of one column block -> fp16 (code - 8) * s, exactly:
+// half 0 gives elements 0-3 (codes at bits 0-3 and 4-7 of each 16-bit half of
+// w), half 1 elements 4-7 (bits 8-11 and 12-15). A rotation brings a code to
+// bits 6-9 of its half, where OR-ed into fp16 16.0 (mantissa unit 1/64) it
+// makes 16 + code; one fma then gives (16 + code) * s - 24 * s. That is exact:
+// s is an 8-bit significand times a power of two, so 24 * s = 8 * (3 * s)
+// needs at most 10 significant bits and the result (code - 8) * s at most 11,
+// and the fma rounds an exact value once. (An offset of 1024 + code would need
+// 1032 * s, 16 bits: only codes at bits 5 or 6 of a half give an offset whose
+// multiple of s fits fp16.) c2 holds -24 * s.
+__device__ __forceinline__ u32x2 dequant_half(uint32_t w, int half, f16x2 s2, f16x2 c2, uint32_t magic) {
+  const uint32_t r0 = __builtin_amdgcn_alignbit(w, w, half ? 2 : 26);   // rotate right
+  const uint32_t r1 = __builtin_amdgcn_alignbit(w, w, half ? 6 : 30);
+  f16x2 t0 = __builtin_bit_cast(f16x2, and_or(r0, kCodeMid, magic));
+  f16x2 t1 = __builtin_bit_cast(f16x2, and_or(r1, kCodeMid, magic));
+  t0 = __builtin_elementwise_fma(t0, s2, c2);
+  t1 = __builtin_elementwise_fma(t1, s2, c2);
+  return u32x2{__builtin_bit_cast(uint32_t, t0), __builtin_bit_cast(uint32_t, t1)};
+}
+
+__device__ __forceinline__ f16x8 join_halves(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
 __device__ __forceinline__ floatx4 mfma16(f16x8 a, f16x8 b, floatx4 c) {
@@ -183,6 +174,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Global -> LDS copy of BYTES per lane (16 or 4) into LDS at `lds` + 4/16 * lane,
+// issued from an asm block: the compiler counts a global_load_lds builtin as
+// a possible LDS access on the LDS counter, and then makes every later LDS
+// read wait for all of them (lgkmcnt(0)) instead of for its own. The copy
+// has no register result (it writes LDS); its address is read at issue. The
+// waits for the copies are explicit (wait_vmcnt), and the "memory" clobber
+// keeps LDS reads on their side of it. M0 holds the LDS base; setting it needs
+// one wait state before the copy. M0 is a register the compiler reserves (it
+// warns about the clobber); no code in this file keeps a value in it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int BYTES, bool NT>
+__device__ __forceinline__ void copy_to_lds(const void* src, const void* lds) {
+  const uint32_t base = (uint32_t)(uintptr_t)LDS_PTR(lds);
+  if (BYTES == 16 && NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(base)
+                 : "memory", "m0");
+  else if (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base)
+                 : "memory", "m0");
+  else if (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(src), "s"(base)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Workgroup barrier without a memory fence. __syncthreads() would make every
 // wave drain all of its in-flight copies first (vmcnt(0)); here each wave has
 // already waited for exactly the copies that must have landed, and the
@@ -216,19 +236,16 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int
   const int g0 = s * kStageGroups;
 #pragma unroll
   for (int j = 0; j < kStageGroups; ++j)
-    __builtin_amdgcn_global_load_lds(c.wq + (int64_t)(g0 + j) * kNibUnitBytes,
-                                     LDS_PTR(base + kBOffset + wave * kBWaveBytes + j * kNibUnitBytes), 16, 0,
-                                     kNonTemporal);
+    copy_to_lds<16, true>(c.wq + (int64_t)(g0 + j) * kNibUnitBytes,
+                          base + kBOffset + wave * kBWaveBytes + j * kNibUnitBytes);
   // the two groups' scale units are adjacent: 64 lanes x 4 bytes cover both
-  __builtin_amdgcn_global_load_lds(c.ws + (int64_t)g0 * (kScaleUnitElems * 2),
-                                   LDS_PTR(base + kSOffset + wave * kSWaveBytes), 4, 0, kNonTemporal);
+  copy_to_lds<4, true>(c.ws + (int64_t)g0 * (kScaleUnitElems * 2), base + kSOffset + wave * kSWaveBytes);
 #pragma unroll
   for (int t = 0; t < nab; ++t)
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) {
       const int rb = nab * wave + t;
-      __builtin_amdgcn_global_load_lds(c.a_src[t] + (int64_t)(g0 + j) * (kGroup * 2),
-                                       LDS_PTR(base + (rb * kStageGroups + j) * 1024), 16, 0, 0);
+      copy_to_lds<16, false>(c.a_src[t] + (int64_t)(g0 + j) * (kGroup * 2), base + (rb * kStageGroups + j) * 1024);
     }
 }
 
@@ -238,7 +255,7 @@ template <int MODE, int NW>
 __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c, uint8_t* ring, int nstages,
                                           int mb, int nb0, int e, int wave, int lane) {
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  uint32_t magic = kF16_1024;
+  uint32_t magic = kF16_16;
   asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "s"(magic));
   floatx4 acc[kRowBlocks][4];
 #pragma unroll
@@ -256,11 +273,21 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     return *reinterpret_cast<const u32x2*>(ring + slot * kStageBytes + kSOffset + wave * kSWaveBytes +
                                            j * (kScaleUnitElems * 2) + 8 * (lane & 15));
   };
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const auto deq = [&](const u32x4& nib, const u32x2& sc, int cb) {
-    const uint32_t sbits = (cb & 2) ? sc.y : sc.x;
+  // -24 * s for the four column blocks' scales of a group (two per word)
+  // (the words are copied out first: a bit cast of a vector element lvalue
+  // compiles to a read of the vector's first element)
+  const auto neg24 = [](const u32x2& sc) {
+    const f16x2 m24 = {(_Float16)-24.0f, (_Float16)-24.0f};
+    const uint32_t lo = sc.x, hi = sc.y;
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) * m24),
+                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) * m24)};
+  };
+  // half h of column block cb's dequantised fragment
+  const auto deqh = [&](const u32x4& nib, const u32x2& sc, const u32x2& cs, int cb, int h) {
+    const uint32_t sbits = (cb & 2) ? sc.y : sc.x, cbits = (cb & 2) ? cs.y : cs.x;
     const f16x2 s2 = splat((cb & 1) ? sbits >> 16 : sbits & 0xFFFFu);
-    return dequant(nib[cb], s2, s2 * sixteenth, magic);
+    const f16x2 c2 = splat((cb & 1) ? cbits >> 16 : cbits & 0xFFFFu);
+    return dequant_half(nib[cb], h, s2, c2, magic);
   };
 
   // the previous tile's reads of every slot are done before it is refilled
@@ -278,8 +305,9 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
   {
     const u32x4 nb = nib_of(0, 0);
     const u32x2 sc = sc_of(0, 0);
+    const u32x2 cs = neg24(sc);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) w[cb] = deq(nb, sc, cb);
+    for (int cb = 0; cb < 4; ++cb) w[cb] = join_halves(deqh(nb, sc, cs, cb, 0), deqh(nb, sc, cs, cb, 1));
   }
 
   for (int s = 0; s < nstages; ++s) {
@@ -303,9 +331,12 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
 #pragma unroll
     for (int rb = 0; rb < kAhead; ++rb) a[rb] = lds_a(rb, 0);
     {
+      // the eight half fragments of the next group, one under each row block's
+      // MFMAs (1.5 VALU per MFMA spread evenly)
       const u32x4 nb = nib1;
       const u32x2 sc = sc1;
-      f16x8 v[4];
+      const u32x2 cs = neg24(sc);
+      u32x2 hv[kRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
         __builtin_amdgcn_sched_barrier(0);
@@ -313,14 +344,15 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
         for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(a[rb], w[cb], acc[rb][cb]);
         if (rb + kAhead < kRowBlocks) a[rb + kAhead] = lds_a(rb + kAhead, 0);
         else a[rb + kAhead - kRowBlocks] = lds_a(rb + kAhead - kRowBlocks, 1);
-        if (rb >= 1 && rb <= 4) v[rb - 1] = deq(nb, sc, rb - 1);
+        hv[rb] = deqh(nb, sc, cs, rb >> 1, rb & 1);
       }
       // keep the dequantisation here, under these MFMAs: without a use in this
       // block the compiler sinks it past the wait below, into the next group
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        asm volatile("" : "+v"(v[cb]));
-        w[cb] = v[cb];
+        f16x8 v = join_halves(hv[2 * cb], hv[2 * cb + 1]);
+        asm volatile("" : "+v"(v));
+        w[cb] = v;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -335,17 +367,21 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
       const u32x2 sc = sc_of(nslot, 0);
       nib1 = nib_of(nslot, 1);
       sc1 = sc_of(nslot, 1);
-      f16x8 v[4];
+      // these nibbles were just read: the first row block's MFMAs cover the
+      // read, and its two halves go under the last row block
+      u32x2 cs, hv[kRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(a[rb], w[cb], acc[rb][cb]);
         if (rb + kAhead < kRowBlocks) a[rb + kAhead] = lds_a(rb + kAhead, 1);
-        if (rb >= 1 && rb <= 4) v[rb - 1] = deq(nb, sc, rb - 1);
+        if (rb == 1) cs = neg24(sc);
+        if (rb >= 1) hv[rb - 1] = deqh(nb, sc, cs, (rb - 1) >> 1, (rb - 1) & 1);
+        if (rb == kRowBlocks - 1) hv[rb] = deqh(nb, sc, cs, rb >> 1, rb & 1);
       }
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) w[cb] = v[cb];
+      for (int cb = 0; cb < 4; ++cb) w[cb] = join_halves(hv[2 * cb], hv[2 * cb + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }

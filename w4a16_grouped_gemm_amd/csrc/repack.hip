@@ -73,8 +73,8 @@ __global__ void repack_scales_kernel(const uint16_t* __restrict__ s, uint16_t* _
 // channel). E_n is the unbiased exponent of the channel's largest |s| minus 4
 // (a zero channel counts as exponent 0, bf16 subnormals as 2^-126), and every
 // group scale is stored as fp16(s * 2^-E_n), a value in (-32, 32): the largest
-// lands in [16, 32), so s / 16, which the tiled GEMM also uses, keeps the
-// range [1, 2) of the largest and stays exact wherever s is.
+// lands in [16, 32), so -24 * s, which the tiled GEMM also uses (at most 10
+// significant bits, magnitude below 768), stays exact wherever s is.
 __global__ void repack_f16_scales_kernel(const uint16_t* __restrict__ s, uint16_t* __restrict__ out,
                                          int32_t* __restrict__ col_exp, int N, int K, int interleave_I,
                                          int64_t total) {
