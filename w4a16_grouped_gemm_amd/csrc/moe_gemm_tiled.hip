@@ -85,9 +85,9 @@ constexpr int a_blocks_per_wave(int nw) { return kRowBlocks / nw; }
 constexpr int copies_per_wave_stage(int nw) { return a_blocks_per_wave(nw) * kStageGroups + kStageGroups + 1; }
 // A fragments read ahead of the MFMAs that use them
 constexpr int kAhead = 4;
-// Weights and scales are read once per tile: copied with the non-temporal
-// policy (operand 2 = nt) so they do not evict the A tile shared through L2.
-constexpr int kNonTemporal = 2;
+// Weights and scales are read once per tile: they are copied with the
+// non-temporal policy (nt) so they do not evict the A tile shared through L2.
+constexpr bool kWeightsNonTemporal = true;
 
 constexpr uint32_t kCodeMid = 0x03C003C0u;  // bits 6-9 of each half
 constexpr uint32_t kF16_16 = 0x4C004C00u;    // fp16 16.0 in both halves
@@ -236,10 +236,10 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* ring, int
   const int g0 = s * kStageGroups;
 #pragma unroll
   for (int j = 0; j < kStageGroups; ++j)
-    copy_to_lds<16, true>(c.wq + (int64_t)(g0 + j) * kNibUnitBytes,
+    copy_to_lds<16, kWeightsNonTemporal>(c.wq + (int64_t)(g0 + j) * kNibUnitBytes,
                           base + kBOffset + wave * kBWaveBytes + j * kNibUnitBytes);
   // the two groups' scale units are adjacent: 64 lanes x 4 bytes cover both
-  copy_to_lds<4, true>(c.ws + (int64_t)g0 * (kScaleUnitElems * 2), base + kSOffset + wave * kSWaveBytes);
+  copy_to_lds<4, kWeightsNonTemporal>(c.ws + (int64_t)g0 * (kScaleUnitElems * 2), base + kSOffset + wave * kSWaveBytes);
 #pragma unroll
   for (int t = 0; t < nab; ++t)
 #pragma unroll
