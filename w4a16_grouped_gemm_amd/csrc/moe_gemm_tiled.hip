@@ -315,6 +315,15 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     // every wave waited for its own copies of stage s before this barrier;
     // everyone also finished reading stage s - 1, whose slot is refilled here
     ring_barrier();
+    // Waves w and w + 4 share a SIMD and its MFMA pipe, and issue ties go to
+    // the older wave: left alone, waves 0-3 reached each stage's barrier about
+    // 850 cycles (a quarter of a stage) before waves 4-7 (per-wave cycle
+    // counters, prefill_contig48). The younger wave leads the first group and
+    // the older one the second, which keeps the pair in step.
+    if (NW == kWaves) {
+      if (wave >= kWaves / 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     if (s + kStages - 1 < nstages) issue_stage(c, ring, (s + kStages - 1) % kStages, s + kStages - 1, wave, a_blocks_per_wave(NW));
 
     // Software pipeline inside the stage: while a group's MFMAs run, the wave
@@ -356,6 +365,10 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (NW == kWaves) {
+      if (wave >= kWaves / 2) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(1);
+    }
     // own copies of stage s + 1 landed (stage s + 2 may still be in flight);
     // after the last stage the reads below see a stale slot whose values are unused
     wait_stage<NW>(min(nstages, s + kStages) - (s + 2));
@@ -386,6 +399,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, const TileCtx& c,
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // Epilogue: rows 16 rb + 4 (lane >> 4) + i of the tile; packed channels
   // 64 nb + 16 cb + (lane & 15).
   const int nb = nb0 + wave;
