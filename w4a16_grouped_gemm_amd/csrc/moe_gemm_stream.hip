@@ -528,7 +528,10 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
 template <int MODE>
 hipError_t launch_mode(int32_t block_m, const GemmParams& p, hipStream_t stream) {
   switch (block_m) {
-    case 16: return launch<MODE, 1, 4, 3>(p, stream);
+    // gate_up's reduction (K = hidden) is long enough to use a 4-deep ring
+    // (3 batches in flight; 3 waves per SIMD); the down projection's shorter
+    // one runs better at 3 deep and 4 waves per SIMD
+    case 16: return MODE == kGateUp ? launch<MODE, 1, 4, 4>(p, stream) : launch<MODE, 1, 4, 3>(p, stream);
     case 32: return launch<MODE, 2, 4, 4>(p, stream);
     case 64: return launch<MODE, 4, 4, 3>(p, stream);
     default: return hipErrorInvalidValue;
@@ -539,7 +542,7 @@ hipError_t launch_mode(int32_t block_m, const GemmParams& p, hipStream_t stream)
 
 hipError_t launch_gate_up_fused_align(const GemmParams& p, const int32_t* ids, int32_t n, int32_t* sorted,
                                       int32_t* expert_ids, int32_t* ntpp, hipStream_t stream) {
-  constexpr int RB = 1, U = 4, DEPTH = 3, KS = 2;
+  constexpr int RB = 1, U = 4, DEPTH = 4, KS = 2;
   using C = Cfg<RB, U, DEPTH, KS>;
   const int G = p.K / kGroup;
   const int NB = p.N / kNBlock;
