@@ -51,10 +51,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 // (a & mask) | magic in one VALU op. gfx9 VOP3 takes no literal and at most one
 // scalar operand, so the mask comes from an SGPR and the magic from a VGPR.
+// (a & mask) | magic, one v_and_or_b32. Plain C, not inline asm: the result
+// feeds an MFMA operand directly, and an MFMA that reads a VGPR needs two wait
+// states after the VALU write of it, which the compiler counts only for
+// instructions it can see (inline asm written there left one).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
+  return (a & mask) | magic;
 }
 
 // Eight stored codes (q + 8) -> eight exact bf16 values q + 136, in k order.

@@ -49,10 +49,12 @@ constexpr uint32_t kBf16_Minus136 = 0xC308C308u;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// (a & mask) | magic, one v_and_or_b32. Plain C, not inline asm: the result
+// feeds an MFMA operand directly, and an MFMA that reads a VGPR needs two wait
+// states after the VALU write of it, which the compiler counts only for
+// instructions it can see (inline asm written there left one).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
+  return (a & mask) | magic;
 }
 
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w, uint32_t magic) {

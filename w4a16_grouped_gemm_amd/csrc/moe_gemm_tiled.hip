@@ -92,6 +92,11 @@ constexpr bool kWeightsNonTemporal = true;
 constexpr uint32_t kCodeMid = 0x03C003C0u;  // bits 6-9 of each half
 constexpr uint32_t kF16_16 = 0x4C004C00u;    // fp16 16.0 in both halves
 
+// (a & mask) | magic as one v_and_or_b32 (in C the compiler folds the rotate
+// before it into other instructions). Its result only ever feeds the fma of
+// dequant_half, a VALU: an MFMA never reads a register this asm writes, so the
+// two wait states an MFMA needs after a VALU write of its operand, which the
+// compiler counts only for instructions it can see, are not at stake here.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
