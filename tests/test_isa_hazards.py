@@ -1,4 +1,4 @@
-"""VALU -> MFMA operand distances in the library's gfx950 device assembly.
+"""Wait states around inline asm in the library's gfx950 device assembly.
 
 An MFMA that reads a VGPR as a source operand needs two wait states (issued
 instructions, or s_nop cycles) after a VALU instruction that wrote that VGPR.
@@ -8,12 +8,13 @@ fed straight into an MFMA can leave too few, and the MFMA then reads the
 register's old contents. The test compiles every kernel source that holds an
 MFMA to assembly with the library's own flags and checks, for each MFMA, the
 last writer of each source register before it, along straight-line code and
-along the branches into its block. Runs on the CPU (hipcc cross-compiles);
-skipped where hipcc is absent.
+along the branches into its block. A second scan checks the inline-asm LDS
+copies: the scalar write of M0 (the copy's LDS address) needs one wait state
+before the copy. Runs on the CPU (hipcc cross-compiles); skipped where hipcc
+is absent.
 """
 from __future__ import annotations
 
-import glob
 import os
 import re
 import shutil
@@ -74,6 +75,28 @@ def _functions(asm: str):
         elif not s.startswith("."):
             cur[1].append(("inst", s))
     return funcs
+
+
+def _writes_m0(inst: str) -> bool:
+    op = inst.split()[0]
+    return op.startswith("s_") and inst[len(op):].split(",")[0].strip() == "m0"
+
+
+def m0_too_close(asm: str):
+    """(function, copy) for each LDS DMA copy (global_load_lds_*) whose M0, the
+    LDS address it writes to, was set by the instruction right before it: a
+    scalar write of M0 needs one wait state before such a copy reads it."""
+    found = []
+    for name, body in _functions(asm):
+        prev = None
+        for kind, v in body:
+            if kind == "label":
+                prev = None
+                continue
+            if v.split()[0].startswith("global_load_lds") and prev is not None and _writes_m0(prev):
+                found.append((name, v))
+            prev = v
+    return found
 
 
 def short_distances(asm: str):
@@ -147,28 +170,63 @@ def test_scanner_flags_a_short_distance():
     assert len(short_distances(branchy)) == 1
 
 
+def test_scanner_flags_an_m0_write_right_before_a_copy():
+    copy = "\tglobal_load_lds_dwordx4 v[2:3], off\n"
+    assert len(m0_too_close("k:\n\ts_mov_b32 m0, s4\n" + copy + ".Lfunc_end0:\n")) == 1
+    assert m0_too_close("k:\n\ts_mov_b32 m0, s4\n\ts_nop 0\n" + copy + ".Lfunc_end0:\n") == []
+    assert m0_too_close("k:\n\ts_mov_b32 s5, s4\n" + copy + ".Lfunc_end0:\n") == []
+
+
+def _lds_dma_sources() -> list[str]:
+    return [s for s in build.sources() if "global_load_lds" in open(s).read()]
+
+
 def _mfma_sources() -> list[str]:
     return [s for s in build.sources() if "mfma" in open(s).read()]
 
 
-@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not found")
-def test_no_short_valu_to_mfma_distance(tmp_path):
+_ASM_CACHE: dict[str, str] = {}
+
+
+def _device_asm(srcs: list[str], tmp_dir) -> dict[str, str]:
+    """gfx950 assembly of each source, compiled with the library's flags."""
     flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
-    srcs = _mfma_sources()
-    assert srcs
 
     def compile_one(src):
-        out = tmp_path / (os.path.basename(src) + ".s")
+        out = os.path.join(str(tmp_dir), os.path.basename(src) + ".s")
         cmd = [HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(build.ROOT, "include"), "-I",
-               os.path.join(build.PKG, "csrc"), src, "-o", str(out)]
+               os.path.join(build.PKG, "csrc"), src, "-o", out]
         res = subprocess.run(cmd, capture_output=True, text=True)
         assert res.returncode == 0, res.stderr[-2000:]
-        return src, out.read_text()
+        return src, open(out).read()
 
-    with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
-        results = list(ex.map(compile_one, srcs))
+    todo = [s for s in srcs if s not in _ASM_CACHE]
+    if todo:
+        with ThreadPoolExecutor(max_workers=min(4, len(todo))) as ex:
+            _ASM_CACHE.update(dict(ex.map(compile_one, todo)))
+    return {s: _ASM_CACHE[s] for s in srcs}
+
+
+needs_hipcc = pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not found")
+
+
+@needs_hipcc
+def test_no_short_valu_to_mfma_distance(tmp_path):
+    srcs = _mfma_sources()
+    assert srcs
     bad = []
-    for src, asm in results:
+    for src, asm in _device_asm(srcs, tmp_path).items():
         assert "v_mfma" in asm, src
         bad += [(os.path.basename(src),) + h for h in short_distances(asm)]
     assert not bad, "\n".join(f"{s} {n[:60]}: {d} wait state(s): {w} -> {m}" for s, n, d, w, m in bad[:10])
+
+
+@needs_hipcc
+def test_m0_set_a_wait_state_before_each_lds_copy(tmp_path):
+    srcs = _lds_dma_sources()
+    assert srcs
+    bad = []
+    for src, asm in _device_asm(srcs, tmp_path).items():
+        assert "global_load_lds" in asm, src
+        bad += [(os.path.basename(src),) + h for h in m0_too_close(asm)]
+    assert not bad, "\n".join(f"{s} {n[:60]}: {c}" for s, n, c in bad[:10])
