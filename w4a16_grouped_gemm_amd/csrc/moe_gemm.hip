@@ -49,12 +49,11 @@ constexpr uint32_t kBf16_Minus136 = 0xC308C308u;  // two bf16 -136.0
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// (a & mask) | magic in one VALU op. gfx9 VOP3 takes no literal and at most one
-// scalar operand, so the mask comes from an SGPR and the magic from a VGPR.
-// (a & mask) | magic, one v_and_or_b32. Plain C, not inline asm: the result
-// feeds an MFMA operand directly, and an MFMA that reads a VGPR needs two wait
-// states after the VALU write of it, which the compiler counts only for
-// instructions it can see (inline asm written there left one).
+// (a & mask) | magic, one v_and_or_b32 (VOP3 takes at most one scalar operand:
+// the mask comes from an SGPR, the magic from a VGPR). Plain C, not inline
+// asm: the result feeds an MFMA operand directly, and an MFMA that reads a
+// VGPR needs two wait states after the VALU write of it, which the compiler
+// counts only for instructions it can see (inline asm written there left one).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
   return (a & mask) | magic;
 }

@@ -5,9 +5,10 @@
 // job is to keep enough of them in flight to run HBM at full rate (decode is
 // HBM-bound; Chord page "vLLM 및 Novita AI, Kimi K2.x용 더 빠른 INT4 MoE 커널
 // 출시: Chord", "핵심 기여" and the latency-tuned buffered-K depth of "그룹 SM90
-// 커널 기법"). The arithmetic is the same as the tiled kernel's: exact integer
-// operands q + 136 on v_mfma_f32_16x16x32_bf16, a -136 * sum(x) correction in
-// the C input, one fp32 FMA per output per 32-wide group for the BF16 scale.
+// 커널 기법"). The arithmetic: exact integer operands q + 136 on
+// v_mfma_f32_16x16x32_bf16, a -136 * sum(x) correction in the C input, one
+// fp32 FMA per output per 32-wide group for the BF16 scale (the tiled kernel
+// instead folds the scale into exact fp16 operands).
 //
 // Work unit: (row block of block_m rows, 4 KN consecutive 64-channel n-blocks)
 // for one 256-thread workgroup; wave w streams n-blocks w KN .. w KN + KN - 1 of
@@ -15,15 +16,15 @@
 // group), so its pipeline runs through KN x K/32 groups without a restart and
 // flushes its accumulators at every n-block boundary. KN > 1 only for short
 // reductions (K/32 groups too few to fill the pipeline, e.g. the down
-// projection of an intermediate-sliced layer). Only the weight nibbles are held in registers: a ring of kDepth
-// batches of U groups, so kDepth - 1 batches (kDepth - 1 KiB x U per wave) are
-// in flight while one is computed. The row block's A fragments (gathered
-// activation rows, shared by the four waves) and each wave's group scales go
-// global -> LDS by global_load_lds (no registers in flight) into rings of the
-// same depth. Copies and loads of a batch are issued together, so the in-order
-// vmcnt covers them all: a wave waits for its own batch, then a fence-free
-// barrier publishes every wave's A copies and proves the slot refilled next
-// has been consumed.
+// projection of an intermediate-sliced layer). Only the weight nibbles are held
+// in registers: a ring of DEPTH batches of U groups, so DEPTH - 1 batches
+// (DEPTH - 1 KiB x U per wave) are in flight while one is computed. The row
+// block's A fragments (gathered activation rows, shared by the four waves) and
+// each wave's group scales go global -> LDS by global_load_lds (no registers in
+// flight) into rings of the same depth. Copies and loads of a batch are issued
+// together, so the in-order vmcnt covers them all: a wave waits for its own
+// batch, then a fence-free barrier publishes every wave's A copies and proves
+// the slot refilled next has been consumed.
 #include "internal.h"
 
 #include <algorithm>
